@@ -1,0 +1,162 @@
+"""Float64 CPU oracle for the DeepSeek Sparse Attention (DSA) hot path.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The product path
+(the C-ABI library and its Python binding) never calls it, and it shares no
+code, constants or tables with the HIP kernels.
+
+What it computes, stage by stage, in the order the pages give:
+
+1. Lightning indexer.  "DeepSeek-V3.2: Pushing the Frontier of Open Large
+   Language Models" (r.nikiv.dev summary), section "How DSA Works": the indexer
+   scores a query against every key, cheaply, in FP8.  The ivugangingo.com
+   article on DeepSeek-V3.2, section "Sparse attention with almost linear
+   long-context costs": a few low-precision indexer heads run on every token
+   pair.  The pages give no formula; this oracle uses
+       score(t, s) = sum_j w[t, j] * ReLU(q[t, j, :] . k[s, :])
+   over the causal pairs s <= pos(t), with q and k the e4m3fn bytes times
+   their per-token fp32 scales, evaluated in float64.
+2. Fine-grained selector.  Same two sections: keep the top-k key positions per
+   query (k = 2048 on the pages).  Ties at the k-th value go to the lowest
+   position; the result is listed in ascending position and padded with -1
+   when fewer than k candidates exist.
+3. Sparse attention.  Same sections, and "Deepseek V3.2 Frontier"
+   (skillmd.com), section "Implementation" for the stage order (score, top-k,
+   gather, softmax-weighted sum): MQA/MLA over the selected rows only.  All
+   heads of a token share one latent KV row per key; the key is the whole
+   row (latent + rope), the value its latent part.
+
+Readings where the pages are silent or garbled (each listed in the design doc):
+the indexer formula and FP8 format; causality (a key is visible iff its
+position <= the query's); the skillmd pseudo-code applies softmax to the
+indexer scores, whereas the ivugangingo article runs a separate MQA/MLA path
+on the selected set -- the oracle follows the article; the value is the
+latent part of the row; -0.0 and +0.0 compare equal.
+
+Nothing here is tuned; every step is the plain definition.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# FP8 e4m3fn decoding (OCP 8-bit floating point, E4M3 "fn" variant)
+# ---------------------------------------------------------------------------
+def e4m3fn_decode(codes) -> np.ndarray:
+    """Decode OCP e4m3fn bytes to float64 by the format's closed form.
+
+    Layout: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits.  Exponent
+    field 0 encodes subnormals (-1)^s * 2^-6 * m/8; otherwise the value is
+    (-1)^s * 2^(e-7) * (1 + m/8).  S.1111.111 is NaN; there is no infinity,
+    so the largest finite magnitude is 2^8 * 1.75 = 448.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64))
+    subnormal = np.ldexp(m / 8.0, -6)
+    val = sign * np.where(e == 0, subnormal, normal)
+    return np.where((e == 0xF) & ((c & 0x7) == 0x7), np.nan, val)
+
+
+def dequantize(codes, scales) -> np.ndarray:
+    """Per-token dequantisation: decoded bytes times one fp32 scale per leading row."""
+    x = e4m3fn_decode(codes)
+    s = np.asarray(scales, dtype=np.float64).reshape((-1,) + (1,) * (x.ndim - 1))
+    return x * s
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """bfloat16 bit patterns (uint16) to float64: the bits are the top half of a float32."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Stage 1: lightning indexer
+# ---------------------------------------------------------------------------
+def indexer_row(q_row: np.ndarray, w_row: np.ndarray, keys: np.ndarray) -> np.ndarray:
+    """Scores of one query against the keys it can see.
+
+    q_row [H_I, d_I] and keys [n, d_I] are dequantised float64; w_row [H_I].
+    Returns sum_j w[j] * max(0, q[j] . k[s]) for each of the n keys.
+    """
+    dots = q_row @ keys.T                       # [H_I, n]: per-head dot products
+    return w_row @ np.maximum(dots, 0.0)        # ReLU, then the w-weighted head sum
+
+
+def indexer_scores(q, w, k, pos) -> list[np.ndarray]:
+    """Causal indexer scores for a set of query rows.
+
+    q [R, H_I, d_I], w [R, H_I], k [S, d_I] float64 (already dequantised);
+    pos[r] is the query's position in its sequence.  Row r sees keys
+    0..pos[r]; the result is a list of R float64 arrays of length pos[r]+1.
+    """
+    return [indexer_row(q[r], w[r], k[: int(pos[r]) + 1]) for r in range(len(pos))]
+
+
+# ---------------------------------------------------------------------------
+# Stage 2: fine-grained top-k selector
+# ---------------------------------------------------------------------------
+def topk_select(scores_row, k: int) -> np.ndarray:
+    """Positions of the k largest scores of one causal row, ascending, -1 padded.
+
+    Candidates are positions 0..n-1 (n = len(scores_row)).  The order is
+    score descending, then position ascending (ties at the threshold go to the
+    lowest position); the first m = min(k, n) are kept and listed in
+    ascending position.  -0.0 and +0.0 are equal under this order.
+    """
+    s = np.asarray(scores_row, dtype=np.float64)
+    n = s.shape[0]
+    order = np.lexsort((np.arange(n), -s))      # primary key: -score, secondary: position
+    m = min(k, n)
+    out = np.full(k, -1, dtype=np.int64)
+    out[:m] = np.sort(order[:m])
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Stage 3: sparse MQA/MLA attention over the selected rows
+# ---------------------------------------------------------------------------
+def sparse_attention_row(q_row, kv, idx, scale: float, d_latent: int):
+    """Attention of one token's H heads over its selected latent KV rows.
+
+    q_row [H, D] and kv [S, D] float64 (D = latent + rope); idx [k] positions
+    into kv, -1 entries skipped.  logits[h, i] = scale * q[h] . kv[idx_i];
+    p = softmax over i; out[h] = sum_i p[h, i] * kv[idx_i, :d_latent];
+    lse[h] = log sum_i exp(logits[h, i]) (natural log).
+    Returns (out [H, d_latent], lse [H]).  With no valid index the output is 0
+    and the lse is -inf.
+    """
+    idx = np.asarray(idx)
+    sel = idx[idx >= 0]
+    H = q_row.shape[0]
+    if sel.size == 0:
+        return np.zeros((H, d_latent)), np.full(H, -np.inf)
+    rows = kv[sel]                              # [m, D] gathered rows
+    logits = scale * (q_row @ rows.T)           # [H, m]
+    mx = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - mx)
+    den = e.sum(axis=1, keepdims=True)
+    out = (e @ rows[:, :d_latent]) / den
+    lse = mx[:, 0] + np.log(den[:, 0])
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# Composition: indexer -> selector -> attention, per query row
+# ---------------------------------------------------------------------------
+def forward_rows(q, w, k, pos, q_attn, kv, topk: int, scale: float, d_latent: int):
+    """DSA for a set of query rows of one sequence, in float64.
+
+    q [R, H_I, d_I], w [R, H_I], k [S, d_I] dequantised; pos [R]; q_attn
+    [R, H, D], kv [S, D].  Returns (scores list, idx [R, k], out [R, H,
+    d_latent], lse [R, H]).
+    """
+    scores = indexer_scores(q, w, k, pos)
+    idx = np.stack([topk_select(s, topk) for s in scores])
+    outs, lses = zip(*(sparse_attention_row(q_attn[r], kv, idx[r], scale, d_latent)
+                       for r in range(len(pos))))
+    return scores, idx, np.stack(outs), np.stack(lses)
