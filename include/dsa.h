@@ -1,0 +1,166 @@
+/*
+ * dsa.h -- C ABI of libdsa.so, the MI355X (gfx950) DeepSeek Sparse Attention
+ * (DSA) hot path: lightning indexer -> top-k selector -> sparse MQA/MLA
+ * attention.
+ *
+ * The method.  The ivugangingo.com article on DeepSeek-V3.2 (section "Sparse
+ * attention with almost linear long-context costs") splits attention into a
+ * lightning indexer -- a few low-precision heads scoring every (query, key)
+ * pair -- and a fine-grained selector that keeps the top-k key positions per
+ * query; the main attention path then runs MQA/MLA on that sparse set only.
+ * The r.nikiv.dev summary ("DeepSeek-V3.2: Pushing the Frontier of Open Large
+ * Language Models", section "How DSA Works") adds that the indexer is FP8 and
+ * that k = 2048.  The pages give no indexer formula; this library computes
+ *     score(t, s) = sum_j w[t, j] * ReLU(q[t, j, :] . k[s, :])
+ * with q, k FP8 e4m3fn (OCP) bytes times per-token fp32 scales, fp32 w and
+ * fp32 accumulation, over causal pairs s <= pos(t).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensors are caller-owned device memory, row-major and contiguous.
+ *   The library never allocates, frees or synchronises; it keeps no state
+ *   besides a thread-local error string.
+ * - Every pointer to device memory must be 16-byte aligned (NULL only where
+ *   an argument is documented as nullable).
+ * - Sequences are packed: sequence b owns query rows
+ *   [q_offsets[b], q_offsets[b+1]) and key/KV rows
+ *   [kv_offsets[b], kv_offsets[b+1]).  Query row r of sequence b sits at
+ *   position pos(r) = q_pos0[b] + (r - q_offsets[b]) and sees the keys at
+ *   positions 0..pos(r) of its own sequence (causal, itself included).
+ *   Required: q_pos0[b] + q_len_b <= kv_len_b.  The offset arrays live on the
+ *   device, so the library cannot check them before launching; kernels clamp
+ *   every index they derive from them to the host-given totals and maxima, so
+ *   inconsistent offsets give wrong results but never an out-of-bounds access.
+ * - FP8 is stored as OCP e4m3fn bytes (uint8_t), bf16 as raw uint16_t bit
+ *   patterns, indices as int32 positions within the sequence.
+ * - Calls are asynchronous on `stream` (a hipStream_t; NULL = default stream).
+ *   Validation runs on the host before anything is enqueued: on a non-OK
+ *   status nothing was launched and dsa_last_error() describes the problem.
+ *   Faults inside kernels surface at the caller's next synchronisation.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARGUMENT = 1, /* null/misaligned pointer, bad size or inconsistent dims */
+  DSA_ERR_UNSUPPORTED = 2,      /* valid request outside the shapes this build supports */
+  DSA_ERR_WORKSPACE = 3,        /* workspace missing or smaller than dsa_workspace_bytes() */
+  DSA_ERR_HIP = 4               /* a HIP runtime call failed (message in dsa_last_error) */
+} dsa_status;
+
+/* Problem description.  A host struct; the three arrays it points to are on
+ * the device.  Scalar totals and maxima are host-known and size the grids. */
+typedef struct dsa_problem {
+  int32_t batch;          /* B >= 1 sequences                                       */
+  int32_t idx_heads;      /* H_I: indexer heads, 1..128                              */
+  int32_t idx_dim;        /* d_I: indexer head width, one of 32, 64, 128             */
+  int32_t heads;          /* H: attention query heads sharing one KV row, 1..128     */
+  int32_t d_latent;       /* value width (latent part of the KV row)                 */
+  int32_t d_rope;         /* rotary part of the KV row (keys only)                   */
+  int32_t topk;           /* k: selected positions per query, 1..4096                */
+  float softmax_scale;    /* attention logit scale, finite and > 0                   */
+  int64_t total_q;        /* packed query rows over all sequences                    */
+  int64_t total_kv;       /* packed key / KV rows over all sequences                 */
+  int64_t max_q_len;      /* >= every q_len_b                                        */
+  int64_t max_kv_len;     /* >= every kv_len_b                                       */
+  const int32_t *q_offsets;  /* device [B+1]: 0 = q_offsets[0] <= ... <= q_offsets[B] = total_q   */
+  const int32_t *kv_offsets; /* device [B+1]: 0 = kv_offsets[0] <= ... <= kv_offsets[B] = total_kv */
+  const int32_t *q_pos0;     /* device [B]: position of each sequence's first query row           */
+} dsa_problem;
+
+/* Workspace selectors for dsa_workspace_bytes(). */
+enum { DSA_WS_TOPK = 0, DSA_WS_ATTN = 1, DSA_WS_FORWARD = 2 };
+
+/*
+ * Stage 1, lightning indexer (r.nikiv.dev summary, "How DSA Works"; the
+ * ivugangingo.com article, "Sparse attention with almost linear long-context
+ * costs").  Writes
+ *   scores[r * ld_scores + s] = q_scale[r] * k_scale[s'] *
+ *       sum_{j < H_I} w[r*H_I + j] * max(0, sum_{d < d_I} q8[r,j,d] * k8[s',d])
+ * for every query row r and every position s <= pos(r), where s' is the
+ * packed key row kv_offsets[b] + s and q8/k8 are the decoded e4m3fn values.
+ * Entries with s > pos(r) are left untouched.  Products are exact in fp32;
+ * accumulation is fp32.
+ *   q_fp8   [total_q, H_I, d_I] uint8   q_scale [total_q] float
+ *   w       [total_q, H_I] float        k_fp8   [total_kv, d_I] uint8
+ *   k_scale [total_kv] float            scores  [total_q, ld_scores] float
+ * ld_scores >= max_kv_len, a multiple of 4.
+ */
+dsa_status dsa_indexer_scores(const dsa_problem *p, const uint8_t *q_fp8, const float *q_scale,
+                              const float *w, const uint8_t *k_fp8, const float *k_scale,
+                              float *scores, int64_t ld_scores, void *stream);
+
+/*
+ * Stage 2, fine-grained top-k selector (same passages).  For each query row r
+ * with n = pos(r) + 1 candidates, writes the m = min(k, n) positions with the
+ * largest scores[r, 0..n-1], in ascending position order, then k - m entries
+ * of -1.  Order: larger score first; equal scores (with -0.0 == +0.0) go to
+ * the lower position.  Scores must not be NaN.
+ *   scores [total_q, ld_scores] float (read on 0..pos(r) only)
+ *   topk_idx [total_q, k] int32
+ * workspace / workspace_bytes: at least dsa_workspace_bytes(p, DSA_WS_TOPK)
+ * bytes of device memory (may be NULL when that is 0).
+ */
+dsa_status dsa_topk(const dsa_problem *p, const float *scores, int64_t ld_scores,
+                    int32_t *topk_idx, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Stage 3, sparse MQA/MLA attention over the selected rows (ivugangingo.com
+ * article, "Sparse attention with almost linear long-context costs"; stage
+ * order as in skillmd.com "Deepseek V3.2 Frontier", "Implementation").  With
+ * D = d_latent + d_rope and, for query row r of sequence b, the valid entries
+ * i of topk_idx[r] (those in [0, kv_len_b); -1 marks padding):
+ *   logit[h, i] = softmax_scale * sum_{d < D} q[r, h, d] * kv[kv_offsets[b] + idx_i, d]
+ *   out[r, h, :] = sum_i softmax_i(logit[h, :]) * kv[kv_offsets[b] + idx_i, 0:d_latent]
+ *   lse[r, h]    = log(sum_i exp(logit[h, i]))     (natural log)
+ * All heads of a token share one gather of its rows.  A row with no valid
+ * index gets out = 0 and lse = -inf.  bf16 inputs, fp32 softmax and
+ * accumulation, bf16 output rounded to nearest even.
+ *   q [total_q, H, D] bf16     kv [total_kv, D] bf16     topk_idx [total_q, k] int32
+ *   out [total_q, H, d_latent] bf16                      lse [total_q, H] float (nullable)
+ * Supported: (d_latent, d_rope) = (512, 64) with H in {32, 64, 128} (the MFMA
+ * path), or any D <= 1024 with H <= 128 (a plain small-shape path, which also
+ * serves other head counts of the 576-wide shape).
+ * workspace: at least dsa_workspace_bytes(p, DSA_WS_ATTN) bytes.
+ */
+dsa_status dsa_sparse_attn(const dsa_problem *p, const uint16_t *q, const uint16_t *kv,
+                           const int32_t *topk_idx, uint16_t *out, float *lse,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The three stages in order (indexer -> top-k -> attention) on one stream.
+ * Arguments as in the stage calls.  The scores matrix lives in the workspace;
+ * topk_idx_out (nullable) receives the selected positions when given,
+ * otherwise they also live in the workspace.
+ * workspace: at least dsa_workspace_bytes(p, DSA_WS_FORWARD) bytes.
+ */
+dsa_status dsa_forward(const dsa_problem *p, const uint8_t *q_fp8, const float *q_scale,
+                       const float *w, const uint8_t *k_fp8, const float *k_scale,
+                       const uint16_t *q, const uint16_t *kv, uint16_t *out, float *lse,
+                       int32_t *topk_idx_out, void *workspace, size_t workspace_bytes,
+                       void *stream);
+
+/* Bytes of device workspace the given entry point needs for problem p
+ * (which = DSA_WS_TOPK, DSA_WS_ATTN or DSA_WS_FORWARD); 0 if none.  Returns
+ * (size_t)-1 for an invalid problem (see dsa_last_error). */
+size_t dsa_workspace_bytes(const dsa_problem *p, int which);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char *dsa_last_error(void);
+
+/* Library version string, e.g. "dsa 0.1.0 gfx950". */
+const char *dsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H_ */

@@ -1,0 +1,259 @@
+"""ctypes binding of libdsa.so (see include/dsa.h): argument marshalling only.
+
+Every entry point takes torch tensors that already live on the GPU, checks
+their dtype / shape / contiguity, and passes raw device pointers and the
+current HIP stream to the C ABI.  All compute happens in the library's HIP
+kernels; there is no fallback.  If libdsa.so is missing or fails to load, the
+first call raises ``DsaLibraryError``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
+_lock = threading.Lock()
+_lib = None
+
+DSA_OK = 0
+DSA_ERR_INVALID_ARGUMENT = 1
+DSA_ERR_UNSUPPORTED = 2
+DSA_ERR_WORKSPACE = 3
+DSA_ERR_HIP = 4
+WS_TOPK, WS_ATTN, WS_FORWARD = 0, 1, 2
+
+EXPORTED = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward",
+            "dsa_workspace_bytes", "dsa_last_error", "dsa_version")
+
+
+class DsaLibraryError(RuntimeError):
+    """libdsa.so is missing or could not be loaded."""
+
+
+class DsaError(RuntimeError):
+    """A libdsa call returned a non-OK status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libdsa status {status}: {message}")
+        self.status = status
+
+
+class DsaProblem(ctypes.Structure):
+    """Mirror of ``dsa_problem`` in include/dsa.h."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("idx_heads", ctypes.c_int32),
+        ("idx_dim", ctypes.c_int32),
+        ("heads", ctypes.c_int32),
+        ("d_latent", ctypes.c_int32),
+        ("d_rope", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+        ("total_q", ctypes.c_int64),
+        ("total_kv", ctypes.c_int64),
+        ("max_q_len", ctypes.c_int64),
+        ("max_kv_len", ctypes.c_int64),
+        ("q_offsets", ctypes.c_void_p),
+        ("kv_offsets", ctypes.c_void_p),
+        ("q_pos0", ctypes.c_void_p),
+    ]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libdsa.so once and declare its signatures."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise DsaLibraryError(
+                f"{_LIB_PATH} is missing: build it with `python -m sparse_attention_18_amd.build`")
+        try:
+            lib = ctypes.CDLL(_LIB_PATH)
+        except OSError as e:
+            raise DsaLibraryError(f"cannot load {_LIB_PATH}: {e}") from e
+        P = ctypes.POINTER(DsaProblem)
+        vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+        lib.dsa_indexer_scores.argtypes = [P, vp, vp, vp, vp, vp, vp, i64, vp]
+        lib.dsa_topk.argtypes = [P, vp, i64, vp, vp, sz, vp]
+        lib.dsa_sparse_attn.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.dsa_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward"):
+            getattr(lib, name).restype = ctypes.c_int
+        lib.dsa_workspace_bytes.argtypes = [P, ctypes.c_int]
+        lib.dsa_workspace_bytes.restype = sz
+        lib.dsa_last_error.argtypes = []
+        lib.dsa_last_error.restype = ctypes.c_char_p
+        lib.dsa_version.argtypes = []
+        lib.dsa_version.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def _check(status: int):
+    if status != DSA_OK:
+        msg = load_library().dsa_last_error().decode(errors="replace")
+        raise DsaError(status, msg)
+
+
+def _ptr(t: torch.Tensor | None, dtype, name: str, shape=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Problem:
+    """A ``dsa_problem`` with its device offset arrays kept alive.
+
+    ``q_offsets`` / ``kv_offsets`` (length B+1) and ``q_pos0`` (length B) are
+    Python lists; they are copied to ``device`` as int32 tensors.
+    """
+
+    def __init__(self, *, q_offsets, kv_offsets, q_pos0, idx_heads, idx_dim, heads,
+                 d_latent, d_rope, topk, softmax_scale, device="cuda"):
+        B = len(q_pos0)
+        if len(q_offsets) != B + 1 or len(kv_offsets) != B + 1:
+            raise ValueError("q_offsets and kv_offsets need batch + 1 entries")
+        self.q_offsets_list = [int(x) for x in q_offsets]
+        self.kv_offsets_list = [int(x) for x in kv_offsets]
+        self.q_pos0_list = [int(x) for x in q_pos0]
+        self._q_off = torch.tensor(self.q_offsets_list, dtype=torch.int32, device=device)
+        self._kv_off = torch.tensor(self.kv_offsets_list, dtype=torch.int32, device=device)
+        self._pos0 = torch.tensor(self.q_pos0_list, dtype=torch.int32, device=device)
+        q_lens = [self.q_offsets_list[i + 1] - self.q_offsets_list[i] for i in range(B)]
+        kv_lens = [self.kv_offsets_list[i + 1] - self.kv_offsets_list[i] for i in range(B)]
+        self.c = DsaProblem(
+            batch=B, idx_heads=idx_heads, idx_dim=idx_dim, heads=heads, d_latent=d_latent,
+            d_rope=d_rope, topk=topk, softmax_scale=softmax_scale,
+            total_q=self.q_offsets_list[-1], total_kv=self.kv_offsets_list[-1],
+            max_q_len=max(q_lens) if q_lens else 0, max_kv_len=max(kv_lens) if kv_lens else 0,
+            q_offsets=self._q_off.data_ptr(), kv_offsets=self._kv_off.data_ptr(),
+            q_pos0=self._pos0.data_ptr())
+
+    @classmethod
+    def from_workload(cls, wl, inputs: dict, device="cuda", q_rows=None, q_pos0=None):
+        """Problem for a workload's generated inputs, optionally restricted to
+        the query rows ``q_rows`` (a slice) of a single sequence starting at
+        position ``q_pos0`` (chunked prefill)."""
+        if q_rows is None:
+            q_off, pos0 = inputs["q_offsets"], inputs["q_pos0"]
+        else:
+            q_off, pos0 = [0, q_rows.stop - q_rows.start], [q_pos0]
+        kv_off = inputs["kv_offsets"]
+        if q_rows is not None:
+            kv_off = [0, q_rows.stop]     # the causal prefix of the chunk
+        return cls(q_offsets=q_off, kv_offsets=kv_off, q_pos0=pos0, idx_heads=wl.idx_heads,
+                   idx_dim=wl.idx_dim, heads=wl.heads, d_latent=wl.d_latent, d_rope=wl.d_rope,
+                   topk=wl.topk, softmax_scale=wl.softmax_scale, device=device)
+
+    @property
+    def total_q(self):
+        return self.c.total_q
+
+    @property
+    def total_kv(self):
+        return self.c.total_kv
+
+    @property
+    def max_kv_len(self):
+        return self.c.max_kv_len
+
+    def ld_scores(self) -> int:
+        """Smallest valid leading dimension for a scores matrix (multiple of 64)."""
+        return max(64, (self.max_kv_len + 63) // 64 * 64)
+
+
+def version() -> str:
+    return load_library().dsa_version().decode()
+
+
+def workspace_bytes(prob: Problem, which: int) -> int:
+    n = load_library().dsa_workspace_bytes(ctypes.byref(prob.c), which)
+    if n == ctypes.c_size_t(-1).value:
+        _check(DSA_ERR_INVALID_ARGUMENT)
+    return int(n)
+
+
+def indexer_scores(prob: Problem, q_fp8, q_scale, w, k_fp8, k_scale, scores, ld=None, stream=None):
+    """Stage 1 (dsa_indexer_scores): writes scores[r, s] for s <= pos(r)."""
+    c = prob.c
+    ld = prob.ld_scores() if ld is None else int(ld)
+    args = (_ptr(q_fp8, torch.uint8, "q_fp8", (c.total_q, c.idx_heads, c.idx_dim)),
+            _ptr(q_scale, torch.float32, "q_scale", (c.total_q,)),
+            _ptr(w, torch.float32, "w", (c.total_q, c.idx_heads)),
+            _ptr(k_fp8, torch.uint8, "k_fp8", (c.total_kv, c.idx_dim)),
+            _ptr(k_scale, torch.float32, "k_scale", (c.total_kv,)),
+            _ptr(scores, torch.float32, "scores", (c.total_q, ld)))
+    _check(load_library().dsa_indexer_scores(ctypes.byref(c), *args, ld, _stream(stream)))
+
+
+def topk(prob: Problem, scores, idx, ld=None, workspace=None, stream=None):
+    """Stage 2 (dsa_topk): ascending top-k positions per query row, -1 padded."""
+    c = prob.c
+    ld = prob.ld_scores() if ld is None else int(ld)
+    ws_ptr = _ptr(workspace, torch.uint8, "workspace") if workspace is not None else None
+    ws_n = workspace.numel() if workspace is not None else 0
+    _check(load_library().dsa_topk(
+        ctypes.byref(c), _ptr(scores, torch.float32, "scores", (c.total_q, ld)), ld,
+        _ptr(idx, torch.int32, "idx", (c.total_q, c.topk)), ws_ptr, ws_n, _stream(stream)))
+
+
+def sparse_attn(prob: Problem, q, kv, idx, out, lse=None, workspace=None, stream=None):
+    """Stage 3 (dsa_sparse_attn): attention of every head over its token's selected rows."""
+    c = prob.c
+    D = c.d_latent + c.d_rope
+    ws_ptr = _ptr(workspace, torch.uint8, "workspace") if workspace is not None else None
+    ws_n = workspace.numel() if workspace is not None else 0
+    _check(load_library().dsa_sparse_attn(
+        ctypes.byref(c), _ptr(q, torch.bfloat16, "q", (c.total_q, c.heads, D)),
+        _ptr(kv, torch.bfloat16, "kv", (c.total_kv, D)),
+        _ptr(idx, torch.int32, "idx", (c.total_q, c.topk)),
+        _ptr(out, torch.bfloat16, "out", (c.total_q, c.heads, c.d_latent)),
+        _ptr(lse, torch.float32, "lse", (c.total_q, c.heads)), ws_ptr, ws_n, _stream(stream)))
+
+
+def forward(prob: Problem, q_fp8, q_scale, w, k_fp8, k_scale, q, kv, out, lse=None,
+            idx_out=None, workspace=None, stream=None):
+    """The three stages in order (dsa_forward); ``workspace`` is a uint8 GPU tensor
+    of at least ``workspace_bytes(prob, WS_FORWARD)`` bytes."""
+    c = prob.c
+    D = c.d_latent + c.d_rope
+    if workspace is None:
+        raise ValueError("forward needs a workspace tensor")
+    _check(load_library().dsa_forward(
+        ctypes.byref(c),
+        _ptr(q_fp8, torch.uint8, "q_fp8", (c.total_q, c.idx_heads, c.idx_dim)),
+        _ptr(q_scale, torch.float32, "q_scale", (c.total_q,)),
+        _ptr(w, torch.float32, "w", (c.total_q, c.idx_heads)),
+        _ptr(k_fp8, torch.uint8, "k_fp8", (c.total_kv, c.idx_dim)),
+        _ptr(k_scale, torch.float32, "k_scale", (c.total_kv,)),
+        _ptr(q, torch.bfloat16, "q", (c.total_q, c.heads, D)),
+        _ptr(kv, torch.bfloat16, "kv", (c.total_kv, D)),
+        _ptr(out, torch.bfloat16, "out", (c.total_q, c.heads, c.d_latent)),
+        _ptr(lse, torch.float32, "lse", (c.total_q, c.heads)),
+        _ptr(idx_out, torch.int32, "idx_out", (c.total_q, c.topk)),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))

@@ -1,0 +1,319 @@
+// C ABI of libdsa.so (declared in include/dsa.h): argument validation on the
+// host, workspace carving and dispatch to the gfx950 kernels.  Nothing is
+// enqueued unless every check passes.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/dsa.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+dsa_status fail(dsa_status st, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return st;
+}
+
+bool aligned16(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+bool aligned4(const void *ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 3u) == 0; }
+
+#define DSA_CHECK(cond, st, ...)              \
+  do {                                        \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+// Checks shared by every entry point.
+dsa_status check_problem(const dsa_problem *p) {
+  DSA_CHECK(p != nullptr, DSA_ERR_INVALID_ARGUMENT, "problem is NULL");
+  DSA_CHECK(p->batch >= 1, DSA_ERR_INVALID_ARGUMENT, "batch must be >= 1 (got %d)", p->batch);
+  DSA_CHECK(p->total_q >= 0 && p->total_kv >= 0, DSA_ERR_INVALID_ARGUMENT,
+            "total_q and total_kv must be >= 0");
+  DSA_CHECK(p->total_q <= INT32_MAX && p->total_kv <= INT32_MAX, DSA_ERR_UNSUPPORTED,
+            "total_q and total_kv must fit int32 row indices");
+  DSA_CHECK(p->max_q_len >= 0 && p->max_q_len <= p->total_q, DSA_ERR_INVALID_ARGUMENT,
+            "max_q_len must be in [0, total_q] (got %lld, total_q %lld)",
+            (long long)p->max_q_len, (long long)p->total_q);
+  DSA_CHECK(p->max_kv_len >= 0 && p->max_kv_len <= p->total_kv, DSA_ERR_INVALID_ARGUMENT,
+            "max_kv_len must be in [0, total_kv] (got %lld, total_kv %lld)",
+            (long long)p->max_kv_len, (long long)p->total_kv);
+  DSA_CHECK(p->q_offsets && p->kv_offsets && p->q_pos0, DSA_ERR_INVALID_ARGUMENT,
+            "q_offsets, kv_offsets and q_pos0 must be non-NULL device arrays");
+  DSA_CHECK(aligned4(p->q_offsets) && aligned4(p->kv_offsets) && aligned4(p->q_pos0),
+            DSA_ERR_INVALID_ARGUMENT, "offset arrays must be 4-byte aligned");
+  DSA_CHECK(p->topk >= 1, DSA_ERR_INVALID_ARGUMENT, "topk must be >= 1 (got %d)", p->topk);
+  DSA_CHECK(p->topk <= 4096, DSA_ERR_UNSUPPORTED, "topk must be <= 4096 (got %d)", p->topk);
+  return DSA_OK;
+}
+
+dsa_status check_indexer_dims(const dsa_problem *p) {
+  DSA_CHECK(p->idx_heads >= 1, DSA_ERR_INVALID_ARGUMENT, "idx_heads must be >= 1");
+  DSA_CHECK(p->idx_heads <= 128, DSA_ERR_UNSUPPORTED, "idx_heads must be <= 128 (got %d)",
+            p->idx_heads);
+  DSA_CHECK(p->idx_dim == 32 || p->idx_dim == 64 || p->idx_dim == 128, DSA_ERR_UNSUPPORTED,
+            "idx_dim must be 32, 64 or 128 (got %d)", p->idx_dim);
+  return DSA_OK;
+}
+
+bool mfma_attn_shape(const dsa_problem *p) {
+  return p->d_latent == 512 && p->d_rope == 64 &&
+         (p->heads == 32 || p->heads == 64 || p->heads == 128);
+}
+
+dsa_status check_attn_dims(const dsa_problem *p) {
+  DSA_CHECK(p->heads >= 1, DSA_ERR_INVALID_ARGUMENT, "heads must be >= 1");
+  DSA_CHECK(p->heads <= 128, DSA_ERR_UNSUPPORTED, "heads must be <= 128 (got %d)", p->heads);
+  DSA_CHECK(p->d_latent >= 1 && p->d_rope >= 0, DSA_ERR_INVALID_ARGUMENT,
+            "d_latent must be >= 1 and d_rope >= 0");
+  DSA_CHECK(mfma_attn_shape(p) || p->d_latent + p->d_rope <= 1024, DSA_ERR_UNSUPPORTED,
+            "d_latent + d_rope must be <= 1024 outside the (512, 64) MFMA shape");
+  DSA_CHECK(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f, DSA_ERR_INVALID_ARGUMENT,
+            "softmax_scale must be finite and > 0");
+  return DSA_OK;
+}
+
+dsa_status check_ld(const dsa_problem *p, int64_t ld) {
+  DSA_CHECK(ld >= p->max_kv_len && ld >= 1, DSA_ERR_INVALID_ARGUMENT,
+            "ld_scores (%lld) must be >= max_kv_len (%lld) and >= 1", (long long)ld,
+            (long long)p->max_kv_len);
+  DSA_CHECK(ld % 4 == 0, DSA_ERR_INVALID_ARGUMENT, "ld_scores must be a multiple of 4");
+  DSA_CHECK(p->total_q == 0 || ld <= INT64_MAX / 4 / p->total_q, DSA_ERR_INVALID_ARGUMENT,
+            "scores matrix size overflows");
+  return DSA_OK;
+}
+
+dsa_status check_ptr(const void *ptr, bool needed, const char *name) {
+  if (!needed) return DSA_OK;
+  DSA_CHECK(ptr != nullptr, DSA_ERR_INVALID_ARGUMENT, "%s is NULL", name);
+  DSA_CHECK(aligned16(ptr), DSA_ERR_INVALID_ARGUMENT, "%s must be 16-byte aligned", name);
+  return DSA_OK;
+}
+
+#define DSA_TRY(expr)                    \
+  do {                                   \
+    dsa_status st_ = (expr);             \
+    if (st_ != DSA_OK) return st_;       \
+  } while (0)
+
+dsa::SeqLayout layout_of(const dsa_problem *p) {
+  dsa::SeqLayout L;
+  L.q_offsets = p->q_offsets;
+  L.kv_offsets = p->kv_offsets;
+  L.q_pos0 = p->q_pos0;
+  L.batch = p->batch;
+  L.total_q = p->total_q;
+  L.total_kv = p->total_kv;
+  L.max_q_len = p->max_q_len;
+  L.max_kv_len = p->max_kv_len;
+  return L;
+}
+
+dsa_status hip_status(hipError_t e, const char *what) {
+  if (e == hipSuccess) return DSA_OK;
+  return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Leading dimension of the scores matrix dsa_forward keeps in its workspace.
+int64_t forward_ld(const dsa_problem *p) {
+  const int64_t n = p->max_kv_len < 1 ? 1 : p->max_kv_len;
+  return (n + 63) / 64 * 64;
+}
+
+dsa::AttnArgs attn_args(const dsa_problem *p, const uint16_t *q, const uint16_t *kv,
+                        const int32_t *idx, uint16_t *out, float *lse, void *ws, size_t wsb) {
+  dsa::AttnArgs a;
+  a.seq = layout_of(p);
+  a.q = q;
+  a.kv = kv;
+  a.idx = idx;
+  a.out = out;
+  a.lse = lse;
+  a.heads = p->heads;
+  a.d_latent = p->d_latent;
+  a.d_rope = p->d_rope;
+  a.k = p->topk;
+  a.scale = p->softmax_scale;
+  a.workspace = ws;
+  a.workspace_bytes = wsb;
+  return a;
+}
+
+dsa::TopkArgs topk_args(const dsa_problem *p, const float *scores, int64_t ld, int32_t *idx) {
+  dsa::TopkArgs a;
+  a.seq = layout_of(p);
+  a.scores = scores;
+  a.ld = ld;
+  a.idx = idx;
+  a.k = p->topk;
+  return a;
+}
+
+dsa::IndexerArgs indexer_args(const dsa_problem *p, const uint8_t *q_fp8, const float *q_scale,
+                              const float *w, const uint8_t *k_fp8, const float *k_scale,
+                              float *scores, int64_t ld) {
+  dsa::IndexerArgs a;
+  a.seq = layout_of(p);
+  a.q_fp8 = q_fp8;
+  a.q_scale = q_scale;
+  a.w = w;
+  a.k_fp8 = k_fp8;
+  a.k_scale = k_scale;
+  a.scores = scores;
+  a.ld = ld;
+  a.idx_heads = p->idx_heads;
+  a.idx_dim = p->idx_dim;
+  return a;
+}
+
+dsa_status check_indexer_ptrs(const dsa_problem *p, const uint8_t *q_fp8, const float *q_scale,
+                              const float *w, const uint8_t *k_fp8, const float *k_scale) {
+  const bool q = p->total_q > 0, k = p->total_kv > 0;
+  DSA_TRY(check_ptr(q_fp8, q, "q_fp8"));
+  DSA_TRY(check_ptr(q_scale, q, "q_scale"));
+  DSA_TRY(check_ptr(w, q, "w"));
+  DSA_TRY(check_ptr(k_fp8, k, "k_fp8"));
+  DSA_TRY(check_ptr(k_scale, k, "k_scale"));
+  return DSA_OK;
+}
+
+dsa_status check_attn_ptrs(const dsa_problem *p, const uint16_t *q, const uint16_t *kv,
+                           uint16_t *out, float *lse) {
+  const bool hq = p->total_q > 0;
+  DSA_TRY(check_ptr(q, hq, "q"));
+  DSA_TRY(check_ptr(kv, p->total_kv > 0, "kv"));
+  DSA_TRY(check_ptr(out, hq, "out"));
+  if (lse != nullptr) DSA_TRY(check_ptr(lse, hq, "lse"));
+  return DSA_OK;
+}
+
+size_t ws_attn(const dsa_problem *p) {
+  return dsa::sparse_attn_workspace_bytes(attn_args(p, nullptr, nullptr, nullptr, nullptr,
+                                                    nullptr, nullptr, 0));
+}
+size_t ws_topk(const dsa_problem *p, int64_t ld) {
+  return dsa::topk_workspace_bytes(topk_args(p, nullptr, ld, nullptr));
+}
+
+// Layout of dsa_forward's workspace: scores | indices | top-k scratch | attention scratch.
+struct ForwardWs {
+  size_t scores, idx, topk, attn, total;
+};
+ForwardWs forward_ws(const dsa_problem *p) {
+  ForwardWs w;
+  const int64_t ld = forward_ld(p);
+  w.scores = round_up((size_t)p->total_q * (size_t)ld * sizeof(float), 256);
+  w.idx = round_up((size_t)p->total_q * (size_t)p->topk * sizeof(int32_t), 256);
+  w.topk = round_up(ws_topk(p, ld), 256);
+  w.attn = round_up(ws_attn(p), 256);
+  w.total = w.scores + w.idx + w.topk + w.attn;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *dsa_last_error(void) { return g_error.c_str(); }
+
+const char *dsa_version(void) { return "dsa 0.1.0 gfx950"; }
+
+size_t dsa_workspace_bytes(const dsa_problem *p, int which) {
+  if (check_problem(p) != DSA_OK) return (size_t)-1;
+  switch (which) {
+    case DSA_WS_TOPK: return ws_topk(p, forward_ld(p));
+    case DSA_WS_ATTN: return ws_attn(p);
+    case DSA_WS_FORWARD: return forward_ws(p).total;
+    default: fail(DSA_ERR_INVALID_ARGUMENT, "unknown workspace selector %d", which); return (size_t)-1;
+  }
+}
+
+dsa_status dsa_indexer_scores(const dsa_problem *p, const uint8_t *q_fp8, const float *q_scale,
+                              const float *w, const uint8_t *k_fp8, const float *k_scale,
+                              float *scores, int64_t ld_scores, void *stream) {
+  DSA_TRY(check_problem(p));
+  DSA_TRY(check_indexer_dims(p));
+  DSA_TRY(check_ld(p, ld_scores));
+  DSA_TRY(check_indexer_ptrs(p, q_fp8, q_scale, w, k_fp8, k_scale));
+  DSA_TRY(check_ptr(scores, p->total_q > 0, "scores"));
+  return hip_status(dsa::launch_indexer(indexer_args(p, q_fp8, q_scale, w, k_fp8, k_scale,
+                                                     scores, ld_scores),
+                                        static_cast<hipStream_t>(stream)),
+                    "indexer launch");
+}
+
+dsa_status dsa_topk(const dsa_problem *p, const float *scores, int64_t ld_scores,
+                    int32_t *topk_idx, void *workspace, size_t workspace_bytes, void *stream) {
+  DSA_TRY(check_problem(p));
+  DSA_TRY(check_ld(p, ld_scores));
+  DSA_TRY(check_ptr(scores, p->total_q > 0, "scores"));
+  DSA_TRY(check_ptr(topk_idx, p->total_q > 0, "topk_idx"));
+  const size_t need = ws_topk(p, ld_scores);
+  DSA_CHECK(workspace_bytes >= need && (need == 0 || workspace != nullptr), DSA_ERR_WORKSPACE,
+            "top-k workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  return hip_status(dsa::launch_topk(topk_args(p, scores, ld_scores, topk_idx),
+                                     static_cast<hipStream_t>(stream)),
+                    "top-k launch");
+}
+
+dsa_status dsa_sparse_attn(const dsa_problem *p, const uint16_t *q, const uint16_t *kv,
+                           const int32_t *topk_idx, uint16_t *out, float *lse, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  DSA_TRY(check_problem(p));
+  DSA_TRY(check_attn_dims(p));
+  DSA_TRY(check_attn_ptrs(p, q, kv, out, lse));
+  DSA_TRY(check_ptr(topk_idx, p->total_q > 0, "topk_idx"));
+  const size_t need = ws_attn(p);
+  DSA_CHECK(workspace_bytes >= need && (need == 0 || workspace != nullptr), DSA_ERR_WORKSPACE,
+            "attention workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  return hip_status(dsa::launch_sparse_attn(attn_args(p, q, kv, topk_idx, out, lse, workspace,
+                                                      workspace_bytes),
+                                            static_cast<hipStream_t>(stream)),
+                    "attention launch");
+}
+
+dsa_status dsa_forward(const dsa_problem *p, const uint8_t *q_fp8, const float *q_scale,
+                       const float *w, const uint8_t *k_fp8, const float *k_scale,
+                       const uint16_t *q, const uint16_t *kv, uint16_t *out, float *lse,
+                       int32_t *topk_idx_out, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+  DSA_TRY(check_problem(p));
+  DSA_TRY(check_indexer_dims(p));
+  DSA_TRY(check_attn_dims(p));
+  DSA_TRY(check_indexer_ptrs(p, q_fp8, q_scale, w, k_fp8, k_scale));
+  DSA_TRY(check_attn_ptrs(p, q, kv, out, lse));
+  if (topk_idx_out != nullptr) DSA_TRY(check_ptr(topk_idx_out, p->total_q > 0, "topk_idx_out"));
+  const ForwardWs ws = forward_ws(p);
+  DSA_CHECK(workspace_bytes >= ws.total && workspace != nullptr, DSA_ERR_WORKSPACE,
+            "forward workspace needs %zu bytes (got %zu)", ws.total, workspace_bytes);
+  DSA_CHECK(aligned16(workspace), DSA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t *base = static_cast<uint8_t *>(workspace);
+  float *scores = reinterpret_cast<float *>(base);
+  int32_t *idx = topk_idx_out != nullptr ? topk_idx_out
+                                         : reinterpret_cast<int32_t *>(base + ws.scores);
+  void *topk_ws = base + ws.scores + ws.idx;
+  void *attn_ws = base + ws.scores + ws.idx + ws.topk;
+  const int64_t ld = forward_ld(p);
+  DSA_TRY(hip_status(dsa::launch_indexer(indexer_args(p, q_fp8, q_scale, w, k_fp8, k_scale,
+                                                      scores, ld), st),
+                     "indexer launch"));
+  DSA_TRY(hip_status(dsa::launch_topk(topk_args(p, scores, ld, idx), st), "top-k launch"));
+  (void)topk_ws;
+  return hip_status(dsa::launch_sparse_attn(attn_args(p, q, kv, idx, out, lse, attn_ws, ws.attn),
+                                            st),
+                    "attention launch");
+}
+
+}  // extern "C"

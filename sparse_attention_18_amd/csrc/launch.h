@@ -1,0 +1,105 @@
+// Internal launch interface between the C-ABI layer (abi.cpp) and the
+// kernel translation units.  Every launcher takes validated arguments and
+// enqueues on `stream`; it returns the hipGetLastError() of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+// Sequence layout shared by all stages (device arrays + host-validated bounds).
+struct SeqLayout {
+  const int32_t *q_offsets;
+  const int32_t *kv_offsets;
+  const int32_t *q_pos0;
+  int32_t batch;
+  int64_t total_q, total_kv, max_q_len, max_kv_len;
+};
+
+struct IndexerArgs {
+  SeqLayout seq;
+  const uint8_t *q_fp8;
+  const float *q_scale;
+  const float *w;
+  const uint8_t *k_fp8;
+  const float *k_scale;
+  float *scores;
+  int64_t ld;
+  int32_t idx_heads, idx_dim;
+};
+
+struct TopkArgs {
+  SeqLayout seq;
+  const float *scores;
+  int64_t ld;
+  int32_t *idx;
+  int32_t k;
+};
+
+struct AttnArgs {
+  SeqLayout seq;
+  const uint16_t *q;
+  const uint16_t *kv;
+  const int32_t *idx;
+  uint16_t *out;
+  float *lse;
+  int32_t heads, d_latent, d_rope, k;
+  float scale;
+  void *workspace;
+  size_t workspace_bytes;
+};
+
+hipError_t launch_indexer(const IndexerArgs &a, hipStream_t stream);
+hipError_t launch_topk(const TopkArgs &a, hipStream_t stream);
+hipError_t launch_sparse_attn(const AttnArgs &a, hipStream_t stream);
+size_t sparse_attn_workspace_bytes(const AttnArgs &a);
+size_t topk_workspace_bytes(const TopkArgs &a);
+
+// Sequence metadata for one sequence, clamped to the host-validated bounds so
+// that inconsistent device offsets can never produce an out-of-bounds access.
+struct SeqInfo {
+  int64_t q0, q1;    // packed query rows [q0, q1)
+  int64_t kv0;       // first packed key row
+  int64_t kvlen;     // keys of this sequence (<= max_kv_len)
+  int64_t pos0;      // position of row q0
+};
+
+__device__ __forceinline__ SeqInfo load_seq(const SeqLayout &L, int b) {
+  SeqInfo s;
+  int64_t q0 = L.q_offsets[b], q1 = L.q_offsets[b + 1];
+  int64_t k0 = L.kv_offsets[b], k1 = L.kv_offsets[b + 1];
+  q0 = q0 < 0 ? 0 : (q0 > L.total_q ? L.total_q : q0);
+  q1 = q1 < q0 ? q0 : (q1 > L.total_q ? L.total_q : q1);
+  k0 = k0 < 0 ? 0 : (k0 > L.total_kv ? L.total_kv : k0);
+  k1 = k1 < k0 ? k0 : (k1 > L.total_kv ? L.total_kv : k1);
+  int64_t kvlen = k1 - k0;
+  if (kvlen > L.max_kv_len) kvlen = L.max_kv_len;
+  int64_t p0 = L.q_pos0[b];
+  p0 = p0 < 0 ? 0 : p0;
+  s.q0 = q0;
+  s.q1 = q1;
+  s.kv0 = k0;
+  s.kvlen = kvlen;
+  s.pos0 = p0;
+  return s;
+}
+
+// Position of packed query row r in sequence s, clamped into [0, kvlen-1]
+// (-1 when the sequence has no keys).
+__device__ __forceinline__ int64_t row_pos(const SeqInfo &s, int64_t r) {
+  int64_t p = s.pos0 + (r - s.q0);
+  return p > s.kvlen - 1 ? s.kvlen - 1 : p;
+}
+
+// Sequence owning packed query row r (binary search over q_offsets).
+__device__ __forceinline__ int find_seq(const SeqLayout &L, int64_t r) {
+  int lo = 0, hi = L.batch - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)L.q_offsets[mid] <= r) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace dsa

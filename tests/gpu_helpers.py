@@ -1,0 +1,93 @@
+"""Shared helpers for the GPU parity tests: run one stage through the C ABI
+and compare it with the float64 oracle on the same inputs.
+
+Tolerances (fixed for this path):
+* indexer scores: |gpu - oracle| <= 1e-3 * max|oracle| over the compared
+  causal entries;
+* top-k: bit-identical to the oracle selector run on the GPU's own scores;
+* attention (given identical indices): max-abs <= 2e-2 and relative
+  Frobenius error <= 1e-2.
+"""
+import numpy as np
+import torch
+
+import oracle
+from sparse_attention_18_amd import binding as dsa
+
+INDEXER_REL_TOL = 1e-3
+ATTN_MAX_ABS = 2e-2
+ATTN_REL_F = 1e-2
+
+
+def to_dev(inp, dev="cuda"):
+    return {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+
+
+def run_indexer(prob, g, rows=None):
+    ld = prob.ld_scores()
+    scores = torch.full((prob.total_q, ld), float("nan"), dtype=torch.float32, device="cuda")
+    dsa.indexer_scores(prob, g["q_fp8"], g["q_scale"], g["w"], g["k_fp8"], g["k_scale"], scores, ld)
+    torch.cuda.synchronize()
+    return scores
+
+
+def oracle_scores_for_rows(inp, q_rows, kv0, positions):
+    """Oracle indexer scores for packed query rows `q_rows` whose keys start at
+    packed key row kv0 and whose positions are `positions`."""
+    qd = oracle.dequantize(inp["q_fp8"][q_rows].numpy(), inp["q_scale"][q_rows].numpy())
+    w = inp["w"][q_rows].double().numpy()
+    n_max = int(max(positions)) + 1
+    kd = oracle.dequantize(inp["k_fp8"][kv0:kv0 + n_max].numpy(),
+                           inp["k_scale"][kv0:kv0 + n_max].numpy())
+    return oracle.indexer_scores(qd, w, kd, positions)
+
+
+def check_indexer_rows(gpu_scores, refs, rows):
+    """Compare GPU score rows (indices `rows` of gpu_scores) with oracle rows."""
+    sc = gpu_scores[rows].cpu().double().numpy()
+    peak = max(np.abs(r).max() for r in refs)
+    err = max(np.abs(sc[i, : len(r)] - r).max() for i, r in enumerate(refs))
+    assert np.isfinite(err) and err <= INDEXER_REL_TOL * peak, \
+        f"indexer max err {err:.3e} > {INDEXER_REL_TOL} * peak {peak:.3e}"
+    return err / peak
+
+
+def check_topk_rows(gpu_idx, gpu_scores, rows, lengths, k):
+    """GPU indices must equal the oracle selector on the GPU's own score rows."""
+    idx = gpu_idx[rows].cpu().numpy()
+    sc = gpu_scores[rows].cpu().double().numpy()
+    for i, n in enumerate(lengths):
+        want = oracle.topk_select(sc[i, :n], k)
+        got = idx[i]
+        if not (got == want).all():
+            bad = np.nonzero(got != want)[0]
+            raise AssertionError(f"top-k mismatch in row {rows[i] if hasattr(rows, '__getitem__') else i}"
+                                 f" (n={n}) at {bad[:8]}: got {got[bad[:8]]} want {want[bad[:8]]}")
+
+
+def check_attention_rows(out, lse, q, kv, idx, rows, kv0s, scale, d_latent):
+    """Oracle attention on the GPU's own indices for the given packed rows."""
+    o_gpu = out[rows].cpu().double().numpy()
+    l_gpu = lse[rows].cpu().double().numpy() if lse is not None else None
+    idx_np = idx[rows].cpu().numpy()
+    refs, lrefs = [], []
+    for i, r in enumerate(rows):
+        kv0 = kv0s[i]
+        sel = idx_np[i]
+        valid = sel[sel >= 0]
+        rows_kv = kv[kv0 + valid].double().numpy() if len(valid) else np.zeros((0, kv.shape[1]))
+        o, l = oracle.sparse_attention_row(q[r].double().numpy(), rows_kv, np.arange(len(valid)),
+                                           scale, d_latent)
+        refs.append(o)
+        lrefs.append(l)
+    ref = np.stack(refs)
+    max_abs = np.abs(o_gpu - ref).max()
+    rel_f = np.linalg.norm(o_gpu - ref) / max(np.linalg.norm(ref), 1e-30)
+    assert max_abs <= ATTN_MAX_ABS and rel_f <= ATTN_REL_F, \
+        f"attention max-abs {max_abs:.3e} relF {rel_f:.3e}"
+    if l_gpu is not None:
+        lref = np.stack(lrefs)
+        fin = np.isfinite(lref)
+        assert (np.isfinite(l_gpu) == fin).all()
+        assert np.abs(l_gpu[fin] - lref[fin]).max() <= 1e-3 * max(1.0, np.abs(lref[fin]).max())
+    return max_abs, rel_f

@@ -1,0 +1,138 @@
+"""The C-ABI library: it loads, exports every entry point include/dsa.h
+declares, and rejects invalid arguments on the host before launching
+anything (so these run without a GPU)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from sparse_attention_18_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa.h")
+FAKE = 0x10000            # 16-byte aligned stand-in device address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(dsa_[a-z_0-9]+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = binding.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(binding.EXPORTED)
+    assert binding.version().startswith("dsa ")
+
+
+def _problem(**kw):
+    base = dict(batch=1, idx_heads=64, idx_dim=128, heads=128, d_latent=512, d_rope=64, topk=2048,
+                softmax_scale=1 / math.sqrt(192), total_q=4096, total_kv=4096, max_q_len=4096,
+                max_kv_len=4096, q_offsets=FAKE, kv_offsets=FAKE, q_pos0=FAKE)
+    base.update(kw)
+    return binding.DsaProblem(**base)
+
+
+def _indexer(p, ld=4096, q=FAKE, scores=FAKE):
+    lib = binding.load_library()
+    return lib.dsa_indexer_scores(ctypes.byref(p) if p is not None else None, q, FAKE, FAKE, FAKE,
+                                  FAKE, scores, ld, None)
+
+
+def _attn(p, out=FAKE):
+    lib = binding.load_library()
+    return lib.dsa_sparse_attn(ctypes.byref(p), FAKE, FAKE, FAKE, out, None, None, 0, None)
+
+
+def _msg():
+    return binding.load_library().dsa_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(batch=0), binding.DSA_ERR_INVALID_ARGUMENT, "batch"),
+    (dict(topk=0), binding.DSA_ERR_INVALID_ARGUMENT, "topk"),
+    (dict(topk=5000), binding.DSA_ERR_UNSUPPORTED, "topk"),
+    (dict(idx_dim=48), binding.DSA_ERR_UNSUPPORTED, "idx_dim"),
+    (dict(idx_heads=0), binding.DSA_ERR_INVALID_ARGUMENT, "idx_heads"),
+    (dict(idx_heads=256), binding.DSA_ERR_UNSUPPORTED, "idx_heads"),
+    (dict(max_q_len=5000), binding.DSA_ERR_INVALID_ARGUMENT, "max_q_len"),
+    (dict(max_kv_len=5000), binding.DSA_ERR_INVALID_ARGUMENT, "max_kv_len"),
+    (dict(q_offsets=None), binding.DSA_ERR_INVALID_ARGUMENT, "offsets"),
+    (dict(kv_offsets=FAKE + 2), binding.DSA_ERR_INVALID_ARGUMENT, "aligned"),
+    (dict(total_q=-1), binding.DSA_ERR_INVALID_ARGUMENT, "total_q"),
+])
+def test_indexer_rejects_bad_problems(kw, status, needle):
+    assert _indexer(_problem(**kw)) == status
+    assert needle in _msg()
+
+
+def test_indexer_rejects_null_problem_bad_ld_and_pointers():
+    lib = binding.load_library()
+    assert lib.dsa_indexer_scores(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4096, None) == \
+        binding.DSA_ERR_INVALID_ARGUMENT
+    assert _indexer(_problem(), ld=4000) == binding.DSA_ERR_INVALID_ARGUMENT
+    assert "ld_scores" in _msg()
+    assert _indexer(_problem(), ld=4098) == binding.DSA_ERR_INVALID_ARGUMENT
+    assert _indexer(_problem(), q=FAKE + 8) == binding.DSA_ERR_INVALID_ARGUMENT
+    assert "q_fp8" in _msg()
+    assert _indexer(_problem(), scores=None) == binding.DSA_ERR_INVALID_ARGUMENT
+    assert "scores" in _msg()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(heads=0), binding.DSA_ERR_INVALID_ARGUMENT, "heads"),
+    (dict(heads=129), binding.DSA_ERR_UNSUPPORTED, "heads"),
+    (dict(d_latent=900, d_rope=200), binding.DSA_ERR_UNSUPPORTED, "1024"),
+    (dict(softmax_scale=float("nan")), binding.DSA_ERR_INVALID_ARGUMENT, "softmax_scale"),
+    (dict(softmax_scale=0.0), binding.DSA_ERR_INVALID_ARGUMENT, "softmax_scale"),
+    (dict(d_latent=0), binding.DSA_ERR_INVALID_ARGUMENT, "d_latent"),
+])
+def test_attention_rejects_bad_problems(kw, status, needle):
+    assert _attn(_problem(**kw)) == status
+    assert needle in _msg()
+
+
+def test_attention_rejects_null_output():
+    assert _attn(_problem(), out=None) == binding.DSA_ERR_INVALID_ARGUMENT
+    assert "out" in _msg()
+
+
+def test_topk_rejects_bad_ld_and_index_pointer():
+    lib = binding.load_library()
+    p = _problem()
+    assert lib.dsa_topk(ctypes.byref(p), FAKE, 100, FAKE, None, 0, None) == \
+        binding.DSA_ERR_INVALID_ARGUMENT
+    assert lib.dsa_topk(ctypes.byref(p), FAKE, 4096, FAKE + 4, None, 0, None) == \
+        binding.DSA_ERR_INVALID_ARGUMENT
+    assert "topk_idx" in _msg()
+
+
+def test_forward_needs_its_workspace():
+    lib = binding.load_library()
+    p = _problem()
+    need = lib.dsa_workspace_bytes(ctypes.byref(p), binding.WS_FORWARD)
+    # scores (4096 x 4096 f32) + indices (4096 x 2048 i32)
+    assert need >= 4096 * 4096 * 4 + 4096 * 2048 * 4
+    st = lib.dsa_forward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                         None, FAKE, need - 1, None)
+    assert st == binding.DSA_ERR_WORKSPACE
+    assert "workspace" in _msg()
+    assert lib.dsa_workspace_bytes(None, binding.WS_FORWARD) == ctypes.c_size_t(-1).value
+    assert lib.dsa_workspace_bytes(ctypes.byref(p), 7) == ctypes.c_size_t(-1).value
+
+
+def test_problem_struct_layout_matches_header():
+    # int32 x7 + float, then four int64, then three pointers
+    assert ctypes.sizeof(binding.DsaProblem) == 8 * 4 + 4 * 8 + 3 * 8
+    assert binding.DsaProblem.total_q.offset == 32
+    assert binding.DsaProblem.q_offsets.offset == 64
