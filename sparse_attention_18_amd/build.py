@@ -22,8 +22,11 @@ ROOT = os.path.dirname(PKG)
 ARCH = "gfx950"
 SOURCES = ["indexer.hip", "topk.hip", "sparse_attn.hip", "abi.cpp"]
 # Packed-FP32 VALU forms are kept out of every device code object.
+# IEEE mode is off (no NaN quieting on min/max): the kernels never rely on
+# signalling-NaN behaviour, and fmaxf then lowers to a single v_max_f32.
 FLAGS = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mno-amdgpu-ieee", "-fno-honor-nans",
          "-Wno-unused-command-line-argument", f"-I{os.path.join(ROOT, 'include')}"]
 
 

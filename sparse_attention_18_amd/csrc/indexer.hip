@@ -43,37 +43,44 @@ struct QueryRegs {
 template <int HB>
 __device__ __forceinline__ void load_query(QueryRegs<HB> &q, const IndexerArgs &p, int64_t row,
                                            bool valid, int g, int c) {
+  // Branch-free: every address is clamped in bounds, invalid parts are zeroed
+  // by selects, so the prologue stays one basic block.
   const int H = p.idx_heads, d = p.idx_dim;
   const float qs = valid ? p.q_scale[row] : 0.0f;
+  const bool dim_ok = 32 * g < d;
+  const int dim_off = dim_ok ? 32 * g : 0;
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) {
     const int head = hb * 16 + c;
-    v4i lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
-    if (valid && head < H && 32 * g < d) {
-      const v4i *src = reinterpret_cast<const v4i *>(p.q_fp8 + (row * H + head) * d + 32 * g);
-      lo = src[0];
-      hi = src[1];
-    }
-    q.a[hb] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    const bool ok = valid && head < H && dim_ok;
+    const v4i *src =
+        reinterpret_cast<const v4i *>(p.q_fp8 + (row * H + (head < H ? head : H - 1)) * d + dim_off);
+    const v4i lo = src[0], hi = src[1];
+    q.a[hb] = ok ? v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}
+                 : v8i{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int h2 = hb * 16 + 4 * g + i;
-      q.w[hb][i] = (valid && h2 < H) ? p.w[row * H + h2] * qs : 0.0f;
+      const float wv = p.w[row * H + (h2 < H ? h2 : H - 1)];
+      q.w[hb][i] = (valid && h2 < H) ? wv * qs : 0.0f;
     }
   }
 }
 
 // sum_j w_j * ReLU(dot_j) over this lane's 4*HB heads for one 16-key block.
+// The HB MFMAs are independent, so they issue back to back before the
+// epilogue consumes them.
 template <int HB>
 __device__ __forceinline__ float score_block(const QueryRegs<HB> &q, const v8i &b) {
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
+  v4f d[HB];
+#pragma unroll
+  for (int hb = 0; hb < HB; ++hb) d[hb] = mfma_16x16x128_fp8(q.a[hb], b, zero);
   float s = 0.f;
 #pragma unroll
-  for (int hb = 0; hb < HB; ++hb) {
-    const v4f d = mfma_16x16x128_fp8(q.a[hb], b, zero);
+  for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s = fmaf(q.w[hb][i], fmaxf(d[i], 0.f), s);
-  }
+    for (int i = 0; i < 4; ++i) s = fmaf(q.w[hb][i], fmaxf(d[hb][i], 0.f), s);
   return s;
 }
 
@@ -89,7 +96,8 @@ __device__ __forceinline__ float reduce_four_blocks(float p0, float p1, float p2
 // rows resident (A operands + weights); the workgroup streams its key range
 // through double-buffered LDS tiles shared by all waves.
 template <int HB, int QW>
-__global__ __launch_bounds__(256) void indexer_prefill_kernel(IndexerArgs p, int key_split) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+void indexer_prefill_kernel(IndexerArgs p, int key_split) {
   constexpr int QT = kWaves * QW;
   __shared__ __attribute__((aligned(16))) uint8_t ktile[2][kKeyTile * kRowBytes];
 
@@ -106,16 +114,16 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(IndexerArgs p, int
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
 
+  // Rows past the end of the tile get zero weights (and are never stored),
+  // so no per-query branch splits the tile loop.
   QueryRegs<HB> q[QW];
   int64_t pos[QW], grow[QW];
-  bool wave_has[QW];
 #pragma unroll
   for (int qi = 0; qi < QW; ++qi) {
     const int64_t r = row_begin + wave * QW + qi;
     const bool valid = r < qlen;
     grow[qi] = s.q0 + (valid ? r : 0);
     pos[qi] = valid ? row_pos(s, grow[qi]) : -1;
-    wave_has[qi] = valid && pos[qi] >= key_begin;
     load_query<HB>(q[qi], p, grow[qi], valid, g, c);
   }
 
@@ -127,9 +135,10 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(IndexerArgs p, int
     for (int e = 0; e < 2; ++e) {
       const int chunk = tid + 256 * e, n = chunk >> 3, j = chunk & 7;
       const int64_t key = t0 + n;
-      stage[e] = v4i{0, 0, 0, 0};
-      if (key < s.kvlen && 16 * j < d)
-        stage[e] = *reinterpret_cast<const v4i *>(p.k_fp8 + (s.kv0 + key) * d + 16 * j);
+      const bool ok = key < s.kvlen && 16 * j < d;
+      const v4i x = *reinterpret_cast<const v4i *>(
+          p.k_fp8 + (s.kv0 + (key < s.kvlen ? key : 0)) * d + (16 * j < d ? 16 * j : 0));
+      stage[e] = ok ? x : v4i{0, 0, 0, 0};
     }
   };
   auto commit = [&](int buf) {
@@ -148,7 +157,7 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(IndexerArgs p, int
     const bool has_next = t0 + kKeyTile < key_end;
     if (has_next) fetch(t0 + kKeyTile);
     const int64_t my_key = t0 + lane;
-    const float ks = my_key < s.kvlen ? p.k_scale[s.kv0 + my_key] : 0.f;
+    const float ks = p.k_scale[s.kv0 + (my_key < s.kvlen ? my_key : 0)];
 
     float part[QW][4];
 #pragma unroll
@@ -158,11 +167,10 @@ __global__ __launch_bounds__(256) void indexer_prefill_kernel(IndexerArgs p, int
       const v4i hi = *reinterpret_cast<const v4i *>(&ktile[buf][ktile_offset(n, 2 * g + 1)]);
       const v8i bop = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-      for (int qi = 0; qi < QW; ++qi) part[qi][kb] = wave_has[qi] ? score_block<HB>(q[qi], bop) : 0.f;
+      for (int qi = 0; qi < QW; ++qi) part[qi][kb] = score_block<HB>(q[qi], bop);
     }
 #pragma unroll
     for (int qi = 0; qi < QW; ++qi) {
-      if (!wave_has[qi]) continue;
       const float v = reduce_four_blocks(part[qi][0], part[qi][1], part[qi][2], part[qi][3]);
       if (my_key < key_end && my_key <= pos[qi]) p.scores[grow[qi] * p.ld + my_key] = v * ks;
     }
@@ -261,7 +269,7 @@ template <int HB>
 hipError_t dispatch(const IndexerArgs &a, hipStream_t stream) {
   // A handful of query rows per sequence: stream keys per row.
   if (a.seq.max_q_len <= 2) return launch_decode<HB>(a, stream);
-  return launch_prefill<HB, (HB >= 4 ? 16 / HB : 4)>(a, stream);
+  return launch_prefill<HB, (HB >= 4 ? 8 / HB : 4)>(a, stream);
 }
 
 }  // namespace

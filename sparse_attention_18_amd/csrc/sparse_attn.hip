@@ -10,10 +10,15 @@
 //
 // MFMA path (d_latent = 512, d_rope = 64, H = 32 * NW heads), one workgroup
 // of NW waves per query token:
-//  * the token's selected rows are gathered 32 at a time straight into LDS
-//    with global_load_lds (16-byte chunks); every head of the token shares
-//    this one gather.  Row pitch 1152 B with the chunk index XOR-swizzled by
-//    (row >> 1) & 7 keeps the MFMA operand reads free of bank conflicts;
+//  * the token's valid indices are compacted once into LDS; its selected
+//    rows are then gathered 32 at a time straight into LDS with LDS-DMA loads
+//    (global_load_lds, 16-byte chunks), three tiles in flight; every head of
+//    the token shares this one gather.  A tile is stored chunk-group major:
+//    16-byte chunk c of row r sits at slot ((c / 8) * 32 + r) * 8 +
+//    ((c % 8) ^ ((r >> 1) & 7)).  One 1 KB DMA load then covers 8 rows x 8
+//    chunks of one group, so a wave's loads need one row index per tile and
+//    immediate offsets, and the MFMA operand reads of 16 consecutive rows hit
+//    16 distinct bank groups;
 //  * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16: wave w takes heads
 //    32w..32w+31 (N), Q^T resident in registers, the 32 keys of the tile as
 //    M and the 576 dims as K;
@@ -40,7 +45,8 @@ constexpr int kChunks = kD * 2 / 16;         // 72 chunks of 16 B per row
 constexpr int kPitch = kChunks * 16;         // 1152 B
 constexpr int kTileBytes = kBN * kPitch;     // 36864 B
 constexpr int kTileInsts = kBN * kChunks / 64;  // 36 wave-wide 1 KB loads per tile
-constexpr int kStages = 2;
+constexpr int kStages = 3;
+constexpr int kMaxK = 4096;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kFrameSlack = 32.f;          // log2 headroom above the frame max
@@ -48,20 +54,52 @@ static_assert(kBN * kChunks % 64 == 0, "tile must be whole 1 KB loads");
 
 __device__ __forceinline__ v8bf as_v8bf(const v4i &x) { return __builtin_bit_cast(v8bf, x); }
 
-// Physical 16-byte slot of logical chunk c in tile row r (self-inverse).
-__device__ __forceinline__ int swz(int r, int c) { return (c & ~7) | ((c ^ (r >> 1)) & 7); }
+// Byte offset, inside a tile, of 16-byte chunk c of row r (see the layout note).
+__device__ __forceinline__ int tile_off(int r, int c) {
+  return (((c >> 3) * kBN + r) * 8 + ((c ^ (r >> 1)) & 7)) * 16;
+}
+
+// One LDS-DMA load: 16 bytes from `g` (per lane) to LDS at lds_base + 16 * lane.
+// Issued from inline assembly so that the compiler does not tie later LDS
+// reads of other tile buffers to its completion; the kernel waits for it
+// explicitly (vmcnt) before the barrier that publishes the tile.  M0 is
+// saved and restored around the load.
+__device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(g), "s"(lds_base)
+      : "memory");
+}
+
+// s_waitcnt on vmcnt only (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
 
 template <int NW>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_sparse_attn_kernel(AttnArgs p) {
   constexpr int H = NW * 32;
+  constexpr int T = NW * 64;                 // threads
   constexpr int DW = kDL / NW;               // latent dims per wave in P.V
   constexpr int MB = DW / 32;                // 32-dim M blocks per wave
+  constexpr int kDmaPerWave = kTileInsts / NW;
   static_assert(DW * NW == kDL && MB * 32 == DW, "latent dims must split evenly over waves");
+  static_assert(kTileInsts % NW == 0, "tile loads must split evenly over waves");
   __shared__ __attribute__((aligned(16))) uint8_t kvbuf[kStages][kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t pbuf[NW * 2 * 1024];
+  __shared__ int idxl[kMaxK];
   __shared__ float lsum[H];
-  __shared__ int s_ntiles, s_flag;
+  __shared__ int s_scan[NW];
+  __shared__ int s_flag;
 
   const int64_t t = blockIdx.x;
   const int b = find_seq(p.seq, t);
@@ -69,62 +107,84 @@ void mla_sparse_attn_kernel(AttnArgs p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = lane >> 5, c32 = lane & 31, jl = lane & 15, half = (lane >> 4) & 1;
   const int k = p.k;
-  const int32_t *idx_row = p.idx + t * k;
   const bool row_ok = t >= s.q0 && t < s.q1;
 
-  // Tiles to visit: up to the last valid index of the row.
-  if (tid == 0) {
-    s_ntiles = 0;
-    s_flag = 0;
-  }
-  __syncthreads();
+  // Compact the row's valid indices (in order) into idxl; m = their count.
+  int m;
   {
-    int last = -1;
-    if (row_ok)
-      for (int i = tid; i < k; i += NW * 64) {
-        const int v = idx_row[i];
-        if (v >= 0 && v < s.kvlen) last = i;
-      }
-    for (int d = 32; d >= 1; d >>= 1) last = max(last, __shfl_xor(last, d, 64));
-    if (lane == 0) atomicMax(&s_ntiles, (last + kBN) / kBN);
+    constexpr int per = kMaxK / T;           // entries per thread (k <= kMaxK)
+    const int32_t *idx_row = p.idx + t * k;
+    const int i0 = tid * per;
+    int vals[per];
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < per; ++e) {
+      const int i = i0 + e;
+      int v = -1;
+      if (row_ok && i < k) v = idx_row[i];
+      vals[e] = (v >= 0 && v < s.kvlen) ? v : -1;
+      cnt += vals[e] >= 0;
+    }
+    int inc = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(inc, d, 64);
+      if (lane >= d) inc += y;
+    }
+    if (lane == 63) s_scan[wave] = inc;
+    if (tid == 0) s_flag = 0;
+    __syncthreads();
+    int base = inc - cnt;
+    m = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) {
+      const int x = s_scan[w2];
+      base += w2 < wave ? x : 0;
+      m += x;
+    }
+#pragma unroll
+    for (int e = 0; e < per; ++e)
+      if (vals[e] >= 0) idxl[base++] = vals[e];
+    __syncthreads();
   }
-  __syncthreads();
-  const int ntiles = s_ntiles;
-
   // Q^T operands of this wave's heads: k-step kk = dims 16kk..16kk+15, lane
-  // (G, c32) holds head 32*wave + c32, dims 16kk + 8G .. +7.
+  // (G, c32) holds head 32*wave + c32, dims 16kk + 8G .. +7.  Row t < total_q
+  // is always in bounds.
   const int head = wave * 32 + c32;
   v8bf qb[kD / 16];
   {
     const uint16_t *qrow = p.q + (t * H + head) * (int64_t)kD + 8 * G;
 #pragma unroll
-    for (int kk = 0; kk < kD / 16; ++kk)   // row t < total_q: always in bounds
+    for (int kk = 0; kk < kD / 16; ++kk)
       qb[kk] = as_v8bf(*reinterpret_cast<const v4i *>(qrow + 16 * kk));
   }
-  const float sl2 = p.scale * kLog2e;
+  const int ntiles = (m + kBN - 1) / kBN;
+  wait_vmcnt<0>();   // Q^T operands resident before any LDS-DMA is in flight
 
-  // Gather tile `tl` (row indices held by lanes 0..31 in `my_idx`).
-  auto gather = [&](int buf, int my_idx, uint32_t vmask) {
-    uint8_t *base = kvbuf[buf];
-    for (int i = wave; i < kTileInsts; i += NW) {
-      const int pch = i * 64 + lane, row = pch / kChunks, slot = pch - row * kChunks;
-      const int gi = __shfl(my_idx, row, 64);
-      const int64_t grow = s.kv0 + (((vmask >> row) & 1u) ? gi : 0);
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const void *>(p.kv + grow * kD + 8 * swz(row, slot)),
-          (DSA_LDS void *)(base + i * 1024), 16, 0, 0);
+  // Gather tile `tl` into its stage buffer; rows past m repeat a valid row.
+  // Load i = wave + NW*ii covers chunk group i/4 of rows 8*(i%4) .. +7: lane
+  // (row 8*(i%4) + lane/8, slot lane%8) receives logical chunk
+  // 8*(i/4) + ((lane%8) ^ f(row)).
+  const uint8_t *kvseq = reinterpret_cast<const uint8_t *>(p.kv + s.kv0 * (int64_t)kD);
+  auto gather = [&](int tl) {
+    const uint32_t base = (uint32_t)(uintptr_t)(DSA_LDS uint8_t *)kvbuf[tl % kStages];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+      if ((rb - wave) % NW != 0) continue;       // this wave's row blocks
+      const int row = 8 * rb + (lane >> 3);
+      const int r = tl * kBN + row;
+      const int gi = idxl[r < m ? r : 0];
+      const uint8_t *src = kvseq + (uint32_t)gi * (uint32_t)(kD * 2) +
+                           16 * ((lane & 7) ^ ((row >> 1) & 7));
+#pragma unroll
+      for (int cg = 0; cg < kChunks / 8; ++cg) {
+        const int i = cg * 4 + rb;
+        lds_dma16(src + 128 * cg, __builtin_amdgcn_readfirstlane(base + i * 1024));
+      }
     }
   };
-  auto fetch_raw = [&](int tl) {
-    const int i = tl * kBN + lane;
-    return (lane < kBN && tl < ntiles && i < k) ? idx_row[i] : -1;
-  };
-  auto validate = [&](int raw, uint32_t &vmask) {
-    const bool valid = raw >= 0 && raw < s.kvlen;
-    vmask = (uint32_t)__ballot(valid);
-    return valid ? raw : 0;
-  };
 
+  const float sl2 = p.scale * kLog2e;
   float m_used = -INFINITY;   // exponent frame of this lane's head (log2 units)
   float m_seen = -INFINITY;   // true running max of this lane's head
   float l_part = 0.f;
@@ -138,57 +198,64 @@ void mla_sparse_attn_kernel(AttnArgs p) {
     l_part = 0.f;
     bool overflow = false;
 
-    uint32_t vm_cur = 0;
-    int raw = -1;
-    if (ntiles > 0) {
-      raw = fetch_raw(0);
-      const int id0 = validate(raw, vm_cur);
-      gather(0, id0, vm_cur);
-      raw = fetch_raw(1);
-    }
+    if (ntiles > 0) gather(0);
+    if (ntiles > 1) gather(1);
     for (int tl = 0; tl < ntiles; ++tl) {
-      const int buf = tl & 1;
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's gathers for tile tl + the index prefetch
-      __syncthreads();                // all gathers landed; P and buffer buf^1 free again
-      const uint32_t vmask = vm_cur;
-      if (tl + 1 < ntiles) {
-        const int id = validate(raw, vm_cur);
-        gather(buf ^ 1, id, vm_cur);
-      }
-      raw = fetch_raw(tl + 2);
-      const uint8_t *tile = kvbuf[buf];
+      // Tile tl's loads are this wave's oldest in flight; tile tl+1's may remain.
+      if (tl + 1 < ntiles) wait_vmcnt<kDmaPerWave>(); else wait_vmcnt<0>();
+      __syncthreads();   // tile tl visible to all; stage (tl+2)%3 and P are free again
+      if (tl + 2 < ntiles) gather(tl + 2);
+      const uint8_t *tile = kvbuf[tl % kStages];
+      const int valid_rows = m - tl * kBN;   // >= 1
 
-      // ---- S^T (32 keys x this wave's 32 heads)
+      // ---- S^T (32 keys x this wave's 32 heads).  Row c32, logical chunk
+      // c = 2kk + G: group kk/4 (immediate offset 4096 * (kk/4)) and one of
+      // four per-lane in-group slots.  Operand reads run three k-steps ahead
+      // of the MFMAs; the scheduling fences stop the compiler from hoisting
+      // all 36 reads at once (which would spill).
       v16f sc = {};
       {
-        const uint8_t *arow = tile + c32 * kPitch;
+        const DSA_LDS uint8_t *tb = (const DSA_LDS uint8_t *)tile;
+        const int x = (c32 >> 1) & 7;
+        const DSA_LDS uint8_t *ab[4];
 #pragma unroll
-        for (int kk = 0; kk < kD / 16; ++kk) {
-          const v4i a = *reinterpret_cast<const v4i *>(arow + 16 * swz(c32, 2 * kk + G));
-          sc = mfma_32x32x16_bf16(as_v8bf(a), qb[kk], sc);
+        for (int j = 0; j < 4; ++j) ab[j] = tb + (c32 * 8 + ((2 * j + G) ^ x)) * 16;
+        auto lda = [&](int kk) {
+          return *reinterpret_cast<const DSA_LDS v4i *>(ab[kk & 3] + (kBN * 8 * 16) * (kk >> 2));
+        };
+        constexpr int KS = kD / 16, LA = 3;
+        v4i a[LA];
+#pragma unroll
+        for (int kk = 0; kk < LA; ++kk) a[kk] = lda(kk);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+          sc = mfma_32x32x16_bf16(as_v8bf(a[kk % LA]), qb[kk], sc);
+          if (kk + LA < KS) a[kk % LA] = lda(kk + LA);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
       // ---- softmax: lane holds keys 8(j/4) + 4G + j%4 of head `head`
       float mt = -INFINITY;
+      const bool partial = valid_rows < kBN;   // only the last tile can be partial
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        const int key = 8 * (j >> 2) + 4 * G + (j & 3);
         float x = sc[j] * sl2;
-        if (!((vmask >> key) & 1u)) x = -INFINITY;
+        if (partial && 8 * (j >> 2) + 4 * G + (j & 3) >= valid_rows) x = -INFINITY;
         sc[j] = x;
         mt = fmaxf(mt, x);
       }
       mt = max_across_halves(mt);
       m_seen = fmaxf(m_seen, mt);
-      if (m_used == -INFINITY) m_used = mt;          // first tile with a valid key
+      if (m_used == -INFINITY) m_used = mt;          // first tile
       overflow |= mt > m_used + kFrameSlack;
-      const float mf = m_used == -INFINITY ? 0.f : m_used;
       v8bf pb[2];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float pe = exp2f(sc[8 * hf + e] - mf);
+          // raw v_exp_f32: arguments below -126 flush to 0, which a softmax
+          // weight that small is anyway next to the frame maximum's 1.0
+          const float pe = __builtin_amdgcn_exp2f(sc[8 * hf + e] - m_used);
           l_part += pe;
           pb[hf][e] = (__bf16)pe;
         }
@@ -197,27 +264,43 @@ void mla_sparse_attn_kernel(AttnArgs p) {
         *reinterpret_cast<v8bf *>(pbuf + ((wave * 2 + hf) * 64 + lane) * 16) = pb[hf];
       __syncthreads();  // P of every head published
 
-      // ---- O^T[dims of this wave][all heads] += V^T . P^T
+      // ---- O^T[dims of this wave][all heads] += V^T . P^T; the transposing
+      // reads for the next 32-dim block are issued before this block's MFMAs.
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        v8bf av[MB];
+        v8bf pbn[NW];
+#pragma unroll
+        for (int nb = 0; nb < NW; ++nb)
+          pbn[nb] = *reinterpret_cast<const v8bf *>(pbuf + ((nb * 2 + hf) * 64 + lane) * 16);
+        // Rows r0 and r1 = r0 + 8; dims d0 = wave*DW + 32u + 16*half + 4*(jl & 3)
+        // lie in logical chunk c = d0/8: group wave*DW/64 + u/2 (immediate),
+        // in-group index 4*(u & 1) + 2*half + ((jl >> 1) & 1), byte (jl & 1)*8.
         const int r0 = 16 * hf + 4 * G + (jl >> 2), r1 = r0 + 8;
+        const int x0 = (r0 >> 1) & 7, x1 = (r1 >> 1) & 7;
+        const int clo = 2 * half + ((jl >> 1) & 1), boff = (jl & 1) * 8;
+        const DSA_LDS uint8_t *tb = (const DSA_LDS uint8_t *)tile + (wave * DW / 64) * (kBN * 8 * 16) + boff;
+        const DSA_LDS uint8_t *vb0[2], *vb1[2];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          vb0[e] = tb + (r0 * 8 + ((4 * e + clo) ^ x0)) * 16;
+          vb1[e] = tb + (r1 * 8 + ((4 * e + clo) ^ x1)) * 16;
+        }
+        auto load_v = [&](int u) {
+          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (DSA_LDS v4s *)(vb0[u & 1] + (kBN * 8 * 16) * (u >> 1)));
+          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (DSA_LDS v4s *)(vb1[u & 1] + (kBN * 8 * 16) * (u >> 1)));
+          const v2i lo2 = __builtin_bit_cast(v2i, lo), hi2 = __builtin_bit_cast(v2i, hi);
+          return as_v8bf(v4i{lo2[0], lo2[1], hi2[0], hi2[1]});
+        };
+        v8bf av[2];
+        av[0] = load_v(0);
 #pragma unroll
         for (int u = 0; u < MB; ++u) {
-          const int d0 = wave * DW + 32 * u + 16 * half + 4 * (jl & 3);
-          const int c = d0 >> 3, off = (d0 & 7) * 2;
-          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (DSA_LDS v4s *)(tile + r0 * kPitch + 16 * swz(r0, c) + off));
-          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (DSA_LDS v4s *)(tile + r1 * kPitch + 16 * swz(r1, c) + off));
-          const v2i lo2 = __builtin_bit_cast(v2i, lo), hi2 = __builtin_bit_cast(v2i, hi);
-          av[u] = as_v8bf(v4i{lo2[0], lo2[1], hi2[0], hi2[1]});
-        }
+          if (u + 1 < MB) av[(u + 1) & 1] = load_v(u + 1);
 #pragma unroll
-        for (int nb = 0; nb < NW; ++nb) {
-          const v8bf pbn = *reinterpret_cast<const v8bf *>(pbuf + ((nb * 2 + hf) * 64 + lane) * 16);
-#pragma unroll
-          for (int u = 0; u < MB; ++u) o[u][nb] = mfma_32x32x16_bf16(av[u], pbn, o[u][nb]);
+          for (int nb = 0; nb < NW; ++nb) o[u][nb] = mfma_32x32x16_bf16(av[u & 1], pbn[nb], o[u][nb]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
