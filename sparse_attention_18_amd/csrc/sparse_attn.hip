@@ -46,6 +46,7 @@ constexpr int kPitch = kChunks * 16;         // 1152 B
 constexpr int kTileBytes = kBN * kPitch;     // 36864 B
 constexpr int kTileInsts = kBN * kChunks / 64;  // 36 wave-wide 1 KB loads per tile
 constexpr int kStages = 3;
+constexpr int kGroupBytes = kBN * 8 * 16;      // one 8-chunk group of a tile
 constexpr int kMaxK = 4096;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -95,16 +96,18 @@ void mla_sparse_attn_kernel(AttnArgs p) {
   static_assert(DW * NW == kDL && MB * 32 == DW, "latent dims must split evenly over waves");
   static_assert(kTileInsts % NW == 0, "tile loads must split evenly over waves");
   __shared__ __attribute__((aligned(16))) uint8_t kvbuf[kStages][kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t pbuf[NW * 2 * 1024];
+  __shared__ __attribute__((aligned(16))) uint8_t pbuf[2][NW * 2 * 1024];
   __shared__ int idxl[kMaxK];
   __shared__ float lsum[H];
   __shared__ int s_scan[NW];
   __shared__ int s_flag;
 
-  const int64_t t = blockIdx.x;
+  // Raw ids: this kernel is large enough that the ockl wrappers behind
+  // blockIdx/threadIdx are not reliably inlined.
+  const int64_t t = __builtin_amdgcn_workgroup_id_x();
   const int b = find_seq(p.seq, t);
   const SeqInfo s = load_seq(p.seq, b);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63, wave = tid >> 6;
   const int G = lane >> 5, c32 = lane & 31, jl = lane & 15, half = (lane >> 4) & 1;
   const int k = p.k;
   const bool row_ok = t >= s.q0 && t < s.q1;
@@ -190,6 +193,28 @@ void mla_sparse_attn_kernel(AttnArgs p) {
   float l_part = 0.f;
   v16f o[MB][NW];
 
+  // Per-lane in-tile byte offsets.  QK operand for k-step kk: row c32,
+  // logical chunk 2kk + G -> group kk/4 (added as an immediate) and in-group
+  // slot (2(kk%4) + G) ^ f(c32).  V^T operand for (hf, u): rows r0 = 16hf +
+  // 4G + jl/4 and r0 + 8, dims wave*DW + 32u + 16*half + 4*(jl%4), i.e. group
+  // wave*DW/64 + u/2, in-group index 4(u%2) + 2*half + (jl/2)%2, byte 8*(jl%2).
+  const int fq = (c32 >> 1) & 7;
+  auto qk_off = [&](int kk) { return (c32 * 8 + ((2 * (kk & 3) + G) ^ fq)) * 16 + kGroupBytes * (kk >> 2); };
+  auto v_off = [&](int hf, int u, int which) {
+    const int r = 16 * hf + 4 * G + (jl >> 2) + 8 * which;
+    const int in = (4 * (u & 1) + 2 * half + ((jl >> 1) & 1)) ^ ((r >> 1) & 7);
+    return (wave * DW / 64 + (u >> 1)) * kGroupBytes + (r * 8 + in) * 16 + (jl & 1) * 8;
+  };
+  auto load_v = [&](const DSA_LDS uint8_t *tb, int hf, int u) {
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS v4s *)(tb + v_off(hf, u, 0)));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS v4s *)(tb + v_off(hf, u, 1)));
+    const v2i lo2 = __builtin_bit_cast(v2i, lo), hi2 = __builtin_bit_cast(v2i, hi);
+    return as_v8bf(v4i{lo2[0], lo2[1], hi2[0], hi2[1]});
+  };
+  auto load_p = [&](const DSA_LDS uint8_t *pb, int hf, int nb) {
+    return *reinterpret_cast<const DSA_LDS v8bf *>(pb + ((nb * 2 + hf) * 64 + lane) * 16);
+  };
+
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
     for (int u = 0; u < MB; ++u)
@@ -198,50 +223,29 @@ void mla_sparse_attn_kernel(AttnArgs p) {
     l_part = 0.f;
     bool overflow = false;
 
-    if (ntiles > 0) gather(0);
-    if (ntiles > 1) gather(1);
-    for (int tl = 0; tl < ntiles; ++tl) {
-      // Tile tl's loads are this wave's oldest in flight; tile tl+1's may remain.
-      if (tl + 1 < ntiles) wait_vmcnt<kDmaPerWave>(); else wait_vmcnt<0>();
-      __syncthreads();   // tile tl visible to all; stage (tl+2)%3 and P are free again
-      if (tl + 2 < ntiles) gather(tl + 2);
-      const uint8_t *tile = kvbuf[tl % kStages];
-      const int valid_rows = m - tl * kBN;   // >= 1
-
-      // ---- S^T (32 keys x this wave's 32 heads).  Row c32, logical chunk
-      // c = 2kk + G: group kk/4 (immediate offset 4096 * (kk/4)) and one of
-      // four per-lane in-group slots.  Operand reads run three k-steps ahead
-      // of the MFMAs; the scheduling fences stop the compiler from hoisting
-      // all 36 reads at once (which would spill).
+    // S^T of tile `tq` and its softmax; publishes P^T into pbuf[tq & 1].
+    auto qk_phase = [&](int tq) {
+      constexpr int KS = kD / 16, LA = 3;
+      const DSA_LDS uint8_t *tbq = (const DSA_LDS uint8_t *)kvbuf[tq % kStages];
       v16f sc = {};
-      {
-        const DSA_LDS uint8_t *tb = (const DSA_LDS uint8_t *)tile;
-        const int x = (c32 >> 1) & 7;
-        const DSA_LDS uint8_t *ab[4];
+      v4i a[LA];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) ab[j] = tb + (c32 * 8 + ((2 * j + G) ^ x)) * 16;
-        auto lda = [&](int kk) {
-          return *reinterpret_cast<const DSA_LDS v4i *>(ab[kk & 3] + (kBN * 8 * 16) * (kk >> 2));
-        };
-        constexpr int KS = kD / 16, LA = 3;
-        v4i a[LA];
+      for (int kk = 0; kk < LA; ++kk) a[kk] = *reinterpret_cast<const DSA_LDS v4i *>(tbq + qk_off(kk));
 #pragma unroll
-        for (int kk = 0; kk < LA; ++kk) a[kk] = lda(kk);
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          sc = mfma_32x32x16_bf16(as_v8bf(a[kk % LA]), qb[kk], sc);
-          if (kk + LA < KS) a[kk % LA] = lda(kk + LA);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+      for (int j = 0; j < KS; ++j) {
+        sc = mfma_32x32x16_bf16(as_v8bf(a[j % LA]), qb[j], sc);
+        if (j + LA < KS) a[j % LA] = *reinterpret_cast<const DSA_LDS v4i *>(tbq + qk_off(j + LA));
+        __builtin_amdgcn_sched_barrier(0);
       }
       // ---- softmax: lane holds keys 8(j/4) + 4G + j%4 of head `head`
+      const int valid_rows = m - tq * kBN;   // >= 1
       float mt = -INFINITY;
-      const bool partial = valid_rows < kBN;   // only the last tile can be partial
+      const bool partial = valid_rows < kBN; // only the last tile can be partial
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        float x = sc[j] * sl2;
-        if (partial && 8 * (j >> 2) + 4 * G + (j & 3) >= valid_rows) x = -INFINITY;
-        sc[j] = x;
+      for (int jj = 0; jj < 16; ++jj) {
+        float x = sc[jj] * sl2;
+        if (partial && 8 * (jj >> 2) + 4 * G + (jj & 3) >= valid_rows) x = -INFINITY;
+        sc[jj] = x;
         mt = fmaxf(mt, x);
       }
       mt = max_across_halves(mt);
@@ -259,49 +263,44 @@ void mla_sparse_attn_kernel(AttnArgs p) {
           l_part += pe;
           pb[hf][e] = (__bf16)pe;
         }
+      uint8_t *pw = pbuf[tq & 1];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
-        *reinterpret_cast<v8bf *>(pbuf + ((wave * 2 + hf) * 64 + lane) * 16) = pb[hf];
-      __syncthreads();  // P of every head published
-
-      // ---- O^T[dims of this wave][all heads] += V^T . P^T; the transposing
-      // reads for the next 32-dim block are issued before this block's MFMAs.
+        *reinterpret_cast<v8bf *>(pw + ((wave * 2 + hf) * 64 + lane) * 16) = pb[hf];
+    };
+    // O^T[dims of this wave][all heads] += V^T . P^T for tile `tp` (P^T read
+    // from pbuf[tp & 1]); V^T operands run one 32-dim block ahead.
+    auto pv_phase = [&](int tp) {
+      const DSA_LDS uint8_t *tbp = (const DSA_LDS uint8_t *)kvbuf[tp % kStages];
+      const DSA_LDS uint8_t *pbp = (const DSA_LDS uint8_t *)pbuf[tp & 1];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        v8bf pbn[NW];
+        v8bf pbn[NW], av[2];
 #pragma unroll
-        for (int nb = 0; nb < NW; ++nb)
-          pbn[nb] = *reinterpret_cast<const v8bf *>(pbuf + ((nb * 2 + hf) * 64 + lane) * 16);
-        // Rows r0 and r1 = r0 + 8; dims d0 = wave*DW + 32u + 16*half + 4*(jl & 3)
-        // lie in logical chunk c = d0/8: group wave*DW/64 + u/2 (immediate),
-        // in-group index 4*(u & 1) + 2*half + ((jl >> 1) & 1), byte (jl & 1)*8.
-        const int r0 = 16 * hf + 4 * G + (jl >> 2), r1 = r0 + 8;
-        const int x0 = (r0 >> 1) & 7, x1 = (r1 >> 1) & 7;
-        const int clo = 2 * half + ((jl >> 1) & 1), boff = (jl & 1) * 8;
-        const DSA_LDS uint8_t *tb = (const DSA_LDS uint8_t *)tile + (wave * DW / 64) * (kBN * 8 * 16) + boff;
-        const DSA_LDS uint8_t *vb0[2], *vb1[2];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          vb0[e] = tb + (r0 * 8 + ((4 * e + clo) ^ x0)) * 16;
-          vb1[e] = tb + (r1 * 8 + ((4 * e + clo) ^ x1)) * 16;
-        }
-        auto load_v = [&](int u) {
-          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (DSA_LDS v4s *)(vb0[u & 1] + (kBN * 8 * 16) * (u >> 1)));
-          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (DSA_LDS v4s *)(vb1[u & 1] + (kBN * 8 * 16) * (u >> 1)));
-          const v2i lo2 = __builtin_bit_cast(v2i, lo), hi2 = __builtin_bit_cast(v2i, hi);
-          return as_v8bf(v4i{lo2[0], lo2[1], hi2[0], hi2[1]});
-        };
-        v8bf av[2];
-        av[0] = load_v(0);
+        for (int nb = 0; nb < NW; ++nb) pbn[nb] = load_p(pbp, hf, nb);
+        av[0] = load_v(tbp, hf, 0);
 #pragma unroll
         for (int u = 0; u < MB; ++u) {
-          if (u + 1 < MB) av[(u + 1) & 1] = load_v(u + 1);
+          if (u + 1 < MB) av[(u + 1) & 1] = load_v(tbp, hf, u + 1);
 #pragma unroll
           for (int nb = 0; nb < NW; ++nb) o[u][nb] = mfma_32x32x16_bf16(av[u & 1], pbn[nb], o[u][nb]);
           __builtin_amdgcn_sched_barrier(0);
         }
+      }
+    };
+
+    // Pipeline: tile t's rows are gathered during step t-1; step t runs QK of
+    // tile t, then P.V of tile t-1.  Three tile buffers: t-1 (P.V), t (QK),
+    // t+1 (in flight); two P buffers.  One barrier per step publishes tile t
+    // and P(t-1) and frees the buffers step t+1 overwrites.
+    if (ntiles > 0) {
+      gather(0);
+      for (int t = 0; t <= ntiles; ++t) {
+        if (t < ntiles) wait_vmcnt<0>();   // this wave's share of tile t landed
+        __syncthreads();                  // tile t and P(t-1) visible; buffer (t+1)%3 free
+        if (t + 1 < ntiles) gather(t + 1);
+        if (t < ntiles) qk_phase(t);
+        if (t > 0) pv_phase(t - 1);
       }
     }
     // A frame overflow anywhere: redo the token in the frame of its true max.
