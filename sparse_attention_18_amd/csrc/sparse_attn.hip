@@ -164,27 +164,28 @@ void mla_sparse_attn_kernel(AttnArgs p) {
   const int ntiles = (m + kBN - 1) / kBN;
   wait_vmcnt<0>();   // Q^T operands resident before any LDS-DMA is in flight
 
-  // Gather tile `tl` into its stage buffer; rows past m repeat a valid row.
-  // Load i = wave + NW*ii covers chunk group i/4 of rows 8*(i%4) .. +7: lane
-  // (row 8*(i%4) + lane/8, slot lane%8) receives logical chunk
-  // 8*(i/4) + ((lane%8) ^ f(row)).
+  // Gather of tile `tl` into its stage buffer; rows past m repeat a valid
+  // row.  Load i covers chunk group i/4 of rows 8*(i%4) .. +7: lane (row
+  // 8*(i%4) + lane/8, slot lane%8) receives logical chunk 8*(i/4) +
+  // ((lane%8) ^ f(row)).  This wave owns row blocks rb = wave + NW*q; its
+  // load d (< kDmaPerWave) is row block q = d / 9, chunk group d % 9.
+  constexpr int kRB = 4 / NW;
+  constexpr int kGroups = kChunks / 8;
   const uint8_t *kvseq = reinterpret_cast<const uint8_t *>(p.kv + s.kv0 * (int64_t)kD);
-  auto gather = [&](int tl) {
-    const uint32_t base = (uint32_t)(uintptr_t)(DSA_LDS uint8_t *)kvbuf[tl % kStages];
+  auto gather_setup = [&](int tl, const uint8_t *(&src)[kRB]) {
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      if ((rb - wave) % NW != 0) continue;       // this wave's row blocks
-      const int row = 8 * rb + (lane >> 3);
+    for (int q = 0; q < kRB; ++q) {
+      const int row = 8 * (wave + NW * q) + (lane >> 3);
       const int r = tl * kBN + row;
       const int gi = idxl[r < m ? r : 0];
-      const uint8_t *src = kvseq + (uint32_t)gi * (uint32_t)(kD * 2) +
-                           16 * ((lane & 7) ^ ((row >> 1) & 7));
-#pragma unroll
-      for (int cg = 0; cg < kChunks / 8; ++cg) {
-        const int i = cg * 4 + rb;
-        lds_dma16(src + 128 * cg, __builtin_amdgcn_readfirstlane(base + i * 1024));
-      }
+      src[q] = kvseq + (uint32_t)gi * (uint32_t)(kD * 2) + 16 * ((lane & 7) ^ ((row >> 1) & 7));
     }
+    return (uint32_t)(uintptr_t)(DSA_LDS uint8_t *)kvbuf[tl % kStages];
+  };
+  auto gather_one = [&](const uint8_t *const (&src)[kRB], uint32_t base, int d) {
+    const int q = d / kGroups, cg = d % kGroups;
+    lds_dma16(src[q] + 128 * cg,
+              __builtin_amdgcn_readfirstlane(base + (cg * 4 + wave + NW * q) * 1024));
   };
 
   const float sl2 = p.scale * kLog2e;
@@ -223,10 +224,15 @@ void mla_sparse_attn_kernel(AttnArgs p) {
     l_part = 0.f;
     bool overflow = false;
 
-    // S^T of tile `tq` and its softmax; publishes P^T into pbuf[tq & 1].
-    auto qk_phase = [&](int tq) {
+    // ---- S^T of tile `tq`; the next tile's gather (when `gnext`) is issued
+    // one load every NW k-steps, in the shadow of the MFMA chain.
+    auto qk_phase = [&](int tq, bool gnext) {
       constexpr int KS = kD / 16, LA = 3;
+      static_assert(KS == NW * kDmaPerWave, "one load per NW k-steps");
       const DSA_LDS uint8_t *tbq = (const DSA_LDS uint8_t *)kvbuf[tq % kStages];
+      const uint8_t *src[kRB];
+      uint32_t gbase = 0;
+      if (gnext) gbase = gather_setup(tq + 1, src);
       v16f sc = {};
       v4i a[LA];
 #pragma unroll
@@ -235,40 +241,49 @@ void mla_sparse_attn_kernel(AttnArgs p) {
       for (int j = 0; j < KS; ++j) {
         sc = mfma_32x32x16_bf16(as_v8bf(a[j % LA]), qb[j], sc);
         if (j + LA < KS) a[j % LA] = *reinterpret_cast<const DSA_LDS v4i *>(tbq + qk_off(j + LA));
+        if (gnext && j % NW == 0) gather_one(src, gbase, j / NW);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // ---- softmax: lane holds keys 8(j/4) + 4G + j%4 of head `head`
+      return sc;
+    };
+
+    // ---- softmax of tile tq: scale + mask + max, frame update, exp2 + sum
+    // + bf16, publish P^T into pbuf[tq & 1].
+    auto sm_scale = [&](v16f &sc, int tq, int j0, int j1, float &mt) {
       const int valid_rows = m - tq * kBN;   // >= 1
-      float mt = -INFINITY;
       const bool partial = valid_rows < kBN; // only the last tile can be partial
 #pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
+      for (int jj = j0; jj < j1; ++jj) {
         float x = sc[jj] * sl2;
         if (partial && 8 * (jj >> 2) + 4 * G + (jj & 3) >= valid_rows) x = -INFINITY;
         sc[jj] = x;
         mt = fmaxf(mt, x);
       }
+    };
+    auto sm_frame = [&](float mt) {
       mt = max_across_halves(mt);
       m_seen = fmaxf(m_seen, mt);
       if (m_used == -INFINITY) m_used = mt;          // first tile
       overflow |= mt > m_used + kFrameSlack;
-      v8bf pb[2];
+    };
+    auto sm_exp = [&](const v16f &sc, v8bf (&pb)[2], int j0, int j1) {
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          // raw v_exp_f32: arguments below -126 flush to 0, which a softmax
-          // weight that small is anyway next to the frame maximum's 1.0
-          const float pe = __builtin_amdgcn_exp2f(sc[8 * hf + e] - m_used);
-          l_part += pe;
-          pb[hf][e] = (__bf16)pe;
-        }
+      for (int jj = j0; jj < j1; ++jj) {
+        // raw v_exp_f32: arguments below -126 flush to 0, which a softmax
+        // weight that small is anyway next to the frame maximum's 1.0
+        const float pe = __builtin_amdgcn_exp2f(sc[jj] - m_used);
+        l_part += pe;
+        pb[jj >> 3][jj & 7] = (__bf16)pe;
+      }
+    };
+    auto sm_store = [&](const v8bf (&pb)[2], int tq) {
       uint8_t *pw = pbuf[tq & 1];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf)
         *reinterpret_cast<v8bf *>(pw + ((wave * 2 + hf) * 64 + lane) * 16) = pb[hf];
     };
-    // O^T[dims of this wave][all heads] += V^T . P^T for tile `tp` (P^T read
+
+    // ---- O^T[dims of this wave][all heads] += V^T . P^T for tile `tp` (P^T
     // from pbuf[tp & 1]); V^T operands run one 32-dim block ahead.
     auto pv_phase = [&](int tp) {
       const DSA_LDS uint8_t *tbp = (const DSA_LDS uint8_t *)kvbuf[tp % kStages];
@@ -290,16 +305,32 @@ void mla_sparse_attn_kernel(AttnArgs p) {
     };
 
     // Pipeline: tile t's rows are gathered during step t-1; step t runs QK of
-    // tile t, then P.V of tile t-1.  Three tile buffers: t-1 (P.V), t (QK),
-    // t+1 (in flight); two P buffers.  One barrier per step publishes tile t
-    // and P(t-1) and frees the buffers step t+1 overwrites.
+    // tile t and its softmax, then P.V of tile t-1.
+    // Three tile buffers: t-1 (P.V), t (QK), t+1 (in flight); two P buffers.
+    // One barrier per step publishes tile t and P(t-1) and frees the buffers
+    // step t+1 overwrites.
     if (ntiles > 0) {
-      gather(0);
+      {
+        const uint8_t *src[kRB];
+        const uint32_t gbase = gather_setup(0, src);
+#pragma unroll
+        for (int d = 0; d < kDmaPerWave; ++d) gather_one(src, gbase, d);
+      }
       for (int t = 0; t <= ntiles; ++t) {
-        if (t < ntiles) wait_vmcnt<0>();   // this wave's share of tile t landed
+        // This wave's share of tile t landed (nothing is in flight at the last
+        // step).  Unconditional, so that the compiler also knows no vector
+        // memory op of its own is pending inside the loop.
+        wait_vmcnt<0>();
         __syncthreads();                  // tile t and P(t-1) visible; buffer (t+1)%3 free
-        if (t + 1 < ntiles) gather(t + 1);
-        if (t < ntiles) qk_phase(t);
+        if (t < ntiles) {
+          v16f sc = qk_phase(t, t + 1 < ntiles);
+          float mt = -INFINITY;
+          v8bf pb[2];
+          sm_scale(sc, t, 0, 16, mt);
+          sm_frame(mt);
+          sm_exp(sc, pb, 0, 16);
+          sm_store(pb, t);
+        }
         if (t > 0) pv_phase(t - 1);
       }
     }
