@@ -7,14 +7,17 @@
 // at the k-th value toward the lower position (-0.0 == +0.0) and pads with -1
 // when a row has fewer than k causal candidates.
 //
-// One 1024-thread workgroup per query row; the row (n = pos+1 fp32 scores) is
+// One 512-thread workgroup per query row (two fit a CU); the row (n = pos+1 fp32 scores) is
 // read once from HBM in the common case:
 //  1. n <= k: every position is selected.
 //  2. Otherwise, a lower bound T_lo on the k-th largest order key comes from
-//     2048 sampled scores (exact select over the sample).  For rows that fit
-//     the candidate buffer (n <= kCap) T_lo is the minimum key, i.e. all.
-//  3. One streaming pass appends every (key, position) with key >= T_lo to an
-//     LDS candidate buffer (wave-aggregated atomics; order not kept).
+//     2048 sampled scores (exact select over the sample): the sample rank is
+//     the expected count above the k-th key plus three standard deviations,
+//     so the candidates number about k plus a margin.  For rows that fit the
+//     candidate buffer (n <= kCap) T_lo is the minimum key, i.e. all.
+//  3. One streaming pass (eight 16-byte loads in flight per thread) appends
+//     every (key, position) with key >= T_lo to an LDS candidate buffer: one
+//     prefix scan and one LDS atomic per wave and step; order not kept.
 //  4. Exact radix select over the candidates gives the k-th key T and the
 //     number of candidates above it.  Because T >= T_lo, every score equal to
 //     T and every score above it is a candidate.
@@ -30,9 +33,10 @@
 namespace dsa {
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 512;
 constexpr int kWavesPerBlock = kThreads / 64;
-constexpr int kCap = 12288;              // candidate buffer entries (key + position)
+constexpr int kCap = 5632;               // candidate buffer entries (key + position); two
+                                         // workgroups' LDS fit one CU
 constexpr int kMaxBitmapN = 131072;      // longest row handled with LDS bitmaps
 constexpr int kBitmapWords = kMaxBitmapN / 32;
 constexpr int kSamples = 2048;           // 64 runs of 32 consecutive scores
@@ -220,7 +224,8 @@ __device__ void select_from_global(const float *row, int64_t n, int k, int32_t *
   }
 }
 
-__global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs p) {
+__global__ __launch_bounds__(kThreads)
+void topk_kernel(TopkArgs p) {
   __shared__ TopkShared sh;
   const int64_t row = blockIdx.x;
   const int b = find_seq(p.seq, row);
@@ -254,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs p) {
     }
     __syncthreads();
     const double expect = (double)kSamples * (double)k / (double)n;
-    int64_t j = (int64_t)(1.5 * expect + 4.0 * sqrt(expect) + 8.0);
+    int64_t j = (int64_t)(expect + 3.0 * sqrt(expect) + 4.0);
     if (j > kSamples) j = kSamples;
     uint32_t n_above_s;
     radix_select([&](int64_t i) { return sh.keys[i]; }, kSamples, (uint32_t)j, sh, t_lo, n_above_s);
@@ -262,31 +267,51 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(TopkArgs p) {
   if (tid == 0) sh.count = 0u;
   __syncthreads();
 
-  // 3. candidate filter: one pass over the row, 4 scores per thread per step
-  for (int64_t base = 0; base < n; base += (int64_t)kThreads * 4) {
-    const int64_t i0 = base + (int64_t)tid * 4;
-    float v[4];
-    if (i0 + 3 < n) {
-      const float4 f = *reinterpret_cast<const float4 *>(rowp + i0);
-      v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
-    } else {
+  // 3. candidate filter: one pass over the row; per step each thread loads
+  // 8 float4 (32 scores, 8 contiguous 16 KB blocks across the workgroup).
+  constexpr int kVec = 8;
+  for (int64_t base = 0; base < n; base += (int64_t)kThreads * 4 * kVec) {
+    float4 v[kVec];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = i0 + e < n ? rowp[i0 + e] : 0.f;
+    for (int e = 0; e < kVec; ++e) {
+      const int64_t i0 = base + ((int64_t)e * kThreads + tid) * 4;
+      if (i0 + 3 < n) {
+        v[e] = *reinterpret_cast<const float4 *>(rowp + i0);
+      } else {
+        v[e].x = i0 + 0 < n ? rowp[i0 + 0] : 0.f;
+        v[e].y = i0 + 1 < n ? rowp[i0 + 1] : 0.f;
+        v[e].z = i0 + 2 < n ? rowp[i0 + 2] : 0.f;
+        v[e].w = i0 + 3 < n ? rowp[i0 + 3] : 0.f;
+      }
     }
+    uint32_t pass_bits = 0u;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t key = order_key(v[e]);
-      const bool pass = (i0 + e < n) && key >= t_lo;
-      const uint64_t m = __ballot(pass);
-      if (m == 0) continue;
-      uint32_t basec = 0;
-      if (lane == 0) basec = atomicAdd(&sh.count, (uint32_t)__popcll(m));
-      basec = __shfl(basec, 0, 64);
-      if (pass) {
-        const uint32_t at = basec + (uint32_t)__popcll(m & ((1ull << lane) - 1ull));
-        if (at < (uint32_t)kCap) {
-          sh.keys[at] = key;
-          sh.pos[at] = (uint32_t)(i0 + e);
+    for (int e = 0; e < kVec; ++e) {
+      const int64_t i0 = base + ((int64_t)e * kThreads + tid) * 4;
+      const float f[4] = {v[e].x, v[e].y, v[e].z, v[e].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (i0 + c < n && order_key(f[c]) >= t_lo) pass_bits |= 1u << (4 * e + c);
+    }
+    const uint32_t cnt = (uint32_t)__popc(pass_bits);
+    const uint32_t inc = wave_inclusive_scan(cnt, lane);
+    uint32_t wbase = 0;
+    if (lane == 63 && inc > 0) wbase = atomicAdd(&sh.count, inc);
+    wbase = __shfl(wbase, 63, 64);
+    uint32_t at = wbase + inc - cnt;
+    // static loop over the 32 slots (a runtime index into v[] would move it
+    // out of registers)
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) {
+      const float f[4] = {v[e].x, v[e].y, v[e].z, v[e].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if ((pass_bits >> (4 * e + c)) & 1u) {
+          if (at < (uint32_t)kCap) {
+            sh.keys[at] = order_key(f[c]);
+            sh.pos[at] = (uint32_t)(base + ((int64_t)e * kThreads + tid) * 4 + c);
+          }
+          ++at;
         }
       }
     }
