@@ -34,11 +34,11 @@ def run_indexer(prob, g, rows=None):
 def oracle_scores_for_rows(inp, q_rows, kv0, positions):
     """Oracle indexer scores for packed query rows `q_rows` whose keys start at
     packed key row kv0 and whose positions are `positions`."""
-    qd = oracle.dequantize(inp["q_fp8"][q_rows].numpy(), inp["q_scale"][q_rows].numpy())
-    w = inp["w"][q_rows].double().numpy()
+    qd = oracle.dequantize(inp["q_fp8"][q_rows].cpu().numpy(), inp["q_scale"][q_rows].cpu().numpy())
+    w = inp["w"][q_rows].cpu().double().numpy()
     n_max = int(max(positions)) + 1
-    kd = oracle.dequantize(inp["k_fp8"][kv0:kv0 + n_max].numpy(),
-                           inp["k_scale"][kv0:kv0 + n_max].numpy())
+    kd = oracle.dequantize(inp["k_fp8"][kv0:kv0 + n_max].cpu().numpy(),
+                           inp["k_scale"][kv0:kv0 + n_max].cpu().numpy())
     return oracle.indexer_scores(qd, w, kd, positions)
 
 
@@ -75,8 +75,9 @@ def check_attention_rows(out, lse, q, kv, idx, rows, kv0s, scale, d_latent):
         kv0 = kv0s[i]
         sel = idx_np[i]
         valid = sel[sel >= 0]
-        rows_kv = kv[kv0 + valid].double().numpy() if len(valid) else np.zeros((0, kv.shape[1]))
-        o, l = oracle.sparse_attention_row(q[r].double().numpy(), rows_kv, np.arange(len(valid)),
+        sel_t = torch.as_tensor(kv0 + valid, dtype=torch.long, device=kv.device)
+        rows_kv = kv[sel_t].cpu().double().numpy() if len(valid) else np.zeros((0, kv.shape[1]))
+        o, l = oracle.sparse_attention_row(q[r].cpu().double().numpy(), rows_kv, np.arange(len(valid)),
                                            scale, d_latent)
         refs.append(o)
         lrefs.append(l)
