@@ -48,6 +48,30 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+_KERNEL_SOURCES = {"sparse_attn": ["sparse_attn.hip", "common.h", "launch.h"],
+                   "indexer": ["indexer.hip", "common.h", "launch.h"],
+                   "topk": ["topk.hip", "common.h", "launch.h"]}
+
+
+def measured_traffic(stage: str):
+    """HBM bytes per launch (read + write) from the committed rocprofv3 counter
+    summary, or None when the kernel's sources changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_chunked_prefill_L131072.json")
+    try:
+        doc = json.load(open(path))
+        rec = doc["kernels"][stage]
+    except (OSError, KeyError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in _KERNEL_SOURCES[stage]:
+        with open(os.path.join(ROOT, "sparse_attention_18_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest()[:16] != rec.get("source_sha256_16"):
+        return None
+    return rec["hbm_read_bytes_per_launch"] + rec["hbm_write_bytes_per_launch"]
+
+
 # ----------------------------------------------------------------- algorithmic work
 def indexer_flops(wl, positions):
     """2 * H_I * d_I flop per causal (query, key) pair."""
@@ -258,6 +282,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--stages-json", default=None, help="also write per-chunk stage times here")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build runs the DSA path on a single "
@@ -267,12 +293,24 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        # A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counters give
+        # the scale from counter units to bytes for the kernels' counters.
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "copies": 3}))
+        return
     dsa.load_library()
     bench, wl, value, ms_per_step, stages, per_chunk = run_prefill(args, dev)
     dominant = max(stages, key=lambda s: stages[s]["ms_per_step"])
     d = stages[dominant]
+    traffic = measured_traffic(dominant)
     roofline = {"bound": d["bound"], "achieved": d["achieved"], "peak": d["peak"],
-                "unit": d["unit"], "frac": d["frac"], "traffic": None, "kernel": dominant}
+                "unit": d["unit"], "frac": d["frac"], "traffic": traffic, "kernel": dominant,
+                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)"}
     decode_us = None
     if not args.no_decode:
         decode_us, _ = run_decode(args, dev)
