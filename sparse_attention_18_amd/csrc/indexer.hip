@@ -15,6 +15,14 @@
 // the head sum is mostly in-lane; the remaining sum over the four 16-lane
 // rows is a permlane reduce-scatter that leaves lane l holding key l of a
 // 64-key block -- one coalesced 256-byte store per query and block.
+//
+// The prefill epilogue uses ReLU(x) = (x + |x|) / 2:
+//     sum_j w_j ReLU(x_j) = sum_j (w_j/2) |x_j|  +  Qe . k,   Qe = sum_j (w_j/2) q_j
+// so each (head, key) result costs one fused multiply-add with an |.| source
+// modifier instead of a max and a multiply-add.  The linear term Qe . k is
+// one more dot product per (query, key); it rides on one extra MFMA per
+// 16-key block whose A rows are Qe split into three e4m3fn pieces
+// (p1 + p2 + p3 = Qe * 2^e, exact up to about 2^-12 of max|Qe|).
 #include "common.h"
 #include "launch.h"
 
@@ -42,11 +50,11 @@ struct QueryRegs {
 
 template <int HB>
 __device__ __forceinline__ void load_query(QueryRegs<HB> &q, const IndexerArgs &p, int64_t row,
-                                           bool valid, int g, int c) {
+                                           bool valid, int g, int c, float wfac) {
   // Branch-free: every address is clamped in bounds, invalid parts are zeroed
   // by selects, so the prologue stays one basic block.
   const int H = p.idx_heads, d = p.idx_dim;
-  const float qs = valid ? p.q_scale[row] : 0.0f;
+  const float qs = valid ? p.q_scale[row] * wfac : 0.0f;
   const bool dim_ok = 32 * g < d;
   const int dim_off = dim_ok ? 32 * g : 0;
 #pragma unroll
@@ -67,21 +75,83 @@ __device__ __forceinline__ void load_query(QueryRegs<HB> &q, const IndexerArgs &
   }
 }
 
-// sum_j w_j * ReLU(dot_j) over this lane's 4*HB heads for one 16-key block.
-// The HB MFMAs are independent, so they issue back to back before the
-// epilogue consumes them.
-template <int HB>
-__device__ __forceinline__ float score_block(const QueryRegs<HB> &q, const v8i &b) {
+// Per-lane head sum over this lane's 4*HB heads for one 16-key block, starting
+// from `s`: sum_j w_j * ReLU(dot_j) (kAbs = false) or sum_j w_j * |dot_j|
+// (kAbs = true, the weights then already carry the factor 1/2).  The HB MFMAs
+// are independent, so they issue back to back before the epilogue uses them.
+template <int HB, bool kAbs>
+__device__ __forceinline__ float score_block(const QueryRegs<HB> &q, const v8i &b, float s) {
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
   v4f d[HB];
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb) d[hb] = mfma_16x16x128_fp8(q.a[hb], b, zero);
-  float s = 0.f;
 #pragma unroll
   for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s = fmaf(q.w[hb][i], fmaxf(d[hb][i], 0.f), s);
+    for (int i = 0; i < 4; ++i)
+      s = fmaf(q.w[hb][i], kAbs ? fabsf(d[hb][i]) : fmaxf(d[hb][i], 0.f), s);
   return s;
+}
+
+constexpr int kLinPieces = 3;  // e4m3fn pieces carrying Qe
+
+// Builds the linear-term operand of this wave's QW queries in LDS:
+//   Qe[d] = sum_j (q_scale * w_j / 2) * q8[j][d]        (fp32)
+//   x = Qe * 2^e with max|x| in [128, 256);  x = p1 + p2 + p3 + tiny rest,
+// each p an e4m3fn vector (the residual after each piece is exact in fp32).
+// `dst` receives the pieces as rows [qi][piece][128 bytes] and `inv` the
+// factor 2^-e per query.  Half-wave h handles query 2r+h in round r; each lane
+// owns 4 consecutive dims.
+template <int QW>
+__device__ __forceinline__ void build_linear_pieces(const IndexerArgs &p, const int64_t (&grow)[QW],
+                                                    const bool (&valid)[QW], int lane,
+                                                    uint8_t *dst, float *inv) {
+  const int H = p.idx_heads, d = p.idx_dim;
+  const int half = lane >> 5, dl = 4 * (lane & 31);
+  const bool dim_ok = dl < d;
+#pragma unroll
+  for (int r = 0; r < (QW + 1) / 2; ++r) {
+    const bool has_pair = 2 * r + 1 < QW;
+    const int qi = 2 * r + half;
+    const bool live = half == 0 || has_pair;
+    const int64_t row = (half && has_pair) ? grow[has_pair ? 2 * r + 1 : 2 * r] : grow[2 * r];
+    const bool ok = live && ((half && has_pair) ? valid[has_pair ? 2 * r + 1 : 2 * r] : valid[2 * r]);
+    const uint8_t *qrow = p.q_fp8 + row * H * d + (dim_ok ? dl : 0);
+    const float *wrow = p.w + row * H;
+    float e0 = 0.f, e1 = 0.f, e2 = 0.f, e3 = 0.f;
+#pragma unroll 16
+    for (int j = 0; j < H; ++j) {
+      const uint32_t x = *reinterpret_cast<const uint32_t *>(qrow + (int64_t)j * d);
+      const float wj = wrow[j];
+      const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(x, 1.0f, false);
+      const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(x, 1.0f, true);
+      e0 = fmaf(wj, lo[0], e0);
+      e1 = fmaf(wj, lo[1], e1);
+      e2 = fmaf(wj, hi[0], e2);
+      e3 = fmaf(wj, hi[1], e3);
+    }
+    const float f = (ok && dim_ok) ? 0.5f * p.q_scale[row] : 0.f;
+    e0 *= f; e1 *= f; e2 *= f; e3 *= f;
+    float m = fmaxf(fmaxf(fabsf(e0), fabsf(e1)), fmaxf(fabsf(e2), fabsf(e3)));
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    // m = f * 2^ex with f in [0.5, 1): scaling by 2^(8 - ex) puts max|x| in [128, 256).
+    const int sh = m > 0.f ? 8 - __builtin_amdgcn_frexp_expf(m) : 0;
+    float x[4] = {ldexpf(e0, sh), ldexpf(e1, sh), ldexpf(e2, sh), ldexpf(e3, sh)};
+#pragma unroll
+    for (int pc = 0; pc < kLinPieces; ++pc) {
+      typedef short v2s __attribute__((ext_vector_type(2)));
+      v2s pk = {0, 0};
+      pk = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(pk, x[0], x[1], 1.0f, false);
+      pk = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(pk, x[2], x[3], 1.0f, true);
+      const uint32_t bits = (uint32_t)(uint16_t)pk[0] | ((uint32_t)(uint16_t)pk[1] << 16);
+      const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(bits, 1.0f, false);
+      const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(bits, 1.0f, true);
+      x[0] -= lo[0]; x[1] -= lo[1]; x[2] -= hi[0]; x[3] -= hi[1];
+      if (live) *reinterpret_cast<uint32_t *>(dst + (qi * kLinPieces + pc) * 128 + dl) = bits;
+    }
+    if (live && (lane & 31) == 0) inv[qi] = ldexpf(1.0f, -sh);
+  }
 }
 
 // Combine the four 16-lane rows' partial sums of four 16-key blocks: lane l
@@ -100,44 +170,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void indexer_prefill_kernel(IndexerArgs p, int key_split) {
   constexpr int QT = kWaves * QW;
   __shared__ __attribute__((aligned(16))) uint8_t ktile[2][kKeyTile * kRowBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t linq[kWaves][QW * kLinPieces * 128];
+  __shared__ float lininv[kWaves][QW];
 
-  const SeqInfo s = load_seq(p.seq, blockIdx.z);
+  const SeqInfo s = load_seq(p.seq, (int)__builtin_amdgcn_workgroup_id_z());
   const int64_t qlen = s.q1 - s.q0;
-  const int64_t row_begin = (int64_t)blockIdx.y * QT;
+  const int64_t row_begin = (int64_t)__builtin_amdgcn_workgroup_id_y() * QT;
   if (row_begin >= qlen || s.kvlen <= 0) return;
   const int64_t rows_here = qlen - row_begin < QT ? qlen - row_begin : QT;
   const int64_t last_pos = row_pos(s, s.q0 + row_begin + rows_here - 1);
-  const int64_t key_begin = (int64_t)blockIdx.x * key_split;
+  // Positions inside one sequence fit in int32 (the offsets are int32).
+  const int key_begin = (int)__builtin_amdgcn_workgroup_id_x() * key_split;
   if (key_begin > last_pos) return;
-  const int64_t key_end = key_begin + key_split < last_pos + 1 ? key_begin + key_split : last_pos + 1;
+  const int key_end = key_begin + key_split < last_pos + 1 ? key_begin + key_split : (int)last_pos + 1;
+  const int kvlen = (int)s.kvlen;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The wave index is uniform; reading it through readfirstlane keeps every
+  // per-query quantity below in scalar registers.
+  const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c = lane & 15;
 
   // Rows past the end of the tile get zero weights (and are never stored),
   // so no per-query branch splits the tile loop.
   QueryRegs<HB> q[QW];
-  int64_t pos[QW], grow[QW];
+  int64_t grow[QW];
+  int pos[QW];
+  bool valid[QW];
 #pragma unroll
   for (int qi = 0; qi < QW; ++qi) {
     const int64_t r = row_begin + wave * QW + qi;
-    const bool valid = r < qlen;
-    grow[qi] = s.q0 + (valid ? r : 0);
-    pos[qi] = valid ? row_pos(s, grow[qi]) : -1;
-    load_query<HB>(q[qi], p, grow[qi], valid, g, c);
+    valid[qi] = r < qlen;
+    grow[qi] = s.q0 + (valid[qi] ? r : 0);
+    pos[qi] = valid[qi] ? (int)row_pos(s, grow[qi]) : -1;
+    load_query<HB>(q[qi], p, grow[qi], valid[qi], g, c, 0.5f);
   }
+  build_linear_pieces<QW>(p, grow, valid, lane, linq[wave], lininv[wave]);
 
   // Each thread stages two 16-byte chunks of a 64-key tile (512 chunks).
   const int d = p.idx_dim;
   v4i stage[2];
-  auto fetch = [&](int64_t t0) {
+  const uint8_t *kbase = p.k_fp8 + s.kv0 * d;
+  auto fetch = [&](int t0) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int chunk = tid + 256 * e, n = chunk >> 3, j = chunk & 7;
-      const int64_t key = t0 + n;
-      const bool ok = key < s.kvlen && 16 * j < d;
+      const int key = t0 + n;
+      const bool ok = key < kvlen && 16 * j < d;
       const v4i x = *reinterpret_cast<const v4i *>(
-          p.k_fp8 + (s.kv0 + (key < s.kvlen ? key : 0)) * d + (16 * j < d ? 16 * j : 0));
+          kbase + (int64_t)(key < kvlen ? key : 0) * d + (16 * j < d ? 16 * j : 0));
       stage[e] = ok ? x : v4i{0, 0, 0, 0};
     }
   };
@@ -152,12 +233,38 @@ void indexer_prefill_kernel(IndexerArgs p, int key_split) {
   fetch(key_begin);
   commit(0);
   __syncthreads();
+
+  // Linear-term A operand: row m = 4*qi + piece (qi < QW, piece < 3), K-chunk
+  // g = dims 32g..32g+31.  The MFMA then leaves query g's three pieces in
+  // elements 0..2 of the 16-lane row g, so `lin_fac[qi]` is 2^-e of query qi
+  // in row qi and zero elsewhere: the reduce-scatter adds the term once.
+  v8i lin_a = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  {
+    const int pq = c >> 2, pc = c & 3;
+    if (pq < QW && pc < kLinPieces) {
+      const uint8_t *src = &linq[wave][(pq * kLinPieces + pc) * 128 + 32 * g];
+      const v4i lo = *reinterpret_cast<const v4i *>(src);
+      const v4i hi = *reinterpret_cast<const v4i *>(src + 16);
+      lin_a = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  }
+  float lin_fac[QW];
+#pragma unroll
+  for (int qi = 0; qi < QW; ++qi) lin_fac[qi] = g == qi ? lininv[wave][qi] : 0.f;
+
   int buf = 0;
-  for (int64_t t0 = key_begin; t0 < key_end; t0 += kKeyTile) {
+  const float *kscale = p.k_scale + s.kv0;
+  float *srow[QW];
+#pragma unroll
+  for (int qi = 0; qi < QW; ++qi) srow[qi] = p.scores + grow[qi] * p.ld;
+  for (int t0 = key_begin; t0 < key_end; t0 += kKeyTile) {
+    // The next tile's loads are clamped in bounds, so they are issued
+    // unconditionally; the stores come last.  Both keep the whole tile body
+    // one basic block, which lets the MFMAs and the epilogue interleave.
     const bool has_next = t0 + kKeyTile < key_end;
-    if (has_next) fetch(t0 + kKeyTile);
-    const int64_t my_key = t0 + lane;
-    const float ks = p.k_scale[s.kv0 + (my_key < s.kvlen ? my_key : 0)];
+    fetch(t0 + kKeyTile);
+    const int my_key = t0 + lane;
+    const float ks = kscale[my_key < kvlen ? my_key : 0];
 
     float part[QW][4];
 #pragma unroll
@@ -166,14 +273,19 @@ void indexer_prefill_kernel(IndexerArgs p, int key_split) {
       const v4i lo = *reinterpret_cast<const v4i *>(&ktile[buf][ktile_offset(n, 2 * g)]);
       const v4i hi = *reinterpret_cast<const v4i *>(&ktile[buf][ktile_offset(n, 2 * g + 1)]);
       const v8i bop = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      const v4f e = mfma_16x16x128_fp8(lin_a, bop, v4f{0.f, 0.f, 0.f, 0.f});
+      const float lin = e[0] + e[1] + e[2];
 #pragma unroll
-      for (int qi = 0; qi < QW; ++qi) part[qi][kb] = score_block<HB>(q[qi], bop);
+      for (int qi = 0; qi < QW; ++qi)
+        part[qi][kb] = score_block<HB, true>(q[qi], bop, lin_fac[qi] * lin);
     }
+    float v[QW];
 #pragma unroll
-    for (int qi = 0; qi < QW; ++qi) {
-      const float v = reduce_four_blocks(part[qi][0], part[qi][1], part[qi][2], part[qi][3]);
-      if (my_key < key_end && my_key <= pos[qi]) p.scores[grow[qi] * p.ld + my_key] = v * ks;
-    }
+    for (int qi = 0; qi < QW; ++qi)
+      v[qi] = reduce_four_blocks(part[qi][0], part[qi][1], part[qi][2], part[qi][3]) * ks;
+#pragma unroll
+    for (int qi = 0; qi < QW; ++qi)
+      if (my_key < key_end && my_key <= pos[qi]) srow[qi][my_key] = v[qi];
     if (has_next) {
       commit(buf ^ 1);
       __syncthreads();
@@ -189,20 +301,20 @@ constexpr int kDecodeChunk = 1024;  // keys per workgroup (4 waves x 256)
 
 template <int HB>
 __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs p) {
-  const int64_t row = blockIdx.y;
+  const int64_t row = __builtin_amdgcn_workgroup_id_y();
   const int b = find_seq(p.seq, row);
   const SeqInfo s = load_seq(p.seq, b);
   if (row < s.q0 || row >= s.q1 || s.kvlen <= 0) return;
   const int64_t pos = row_pos(s, row);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int64_t wave_begin = (int64_t)blockIdx.x * kDecodeChunk + wave * (kDecodeChunk / kWaves);
+  const int64_t wave_begin = (int64_t)__builtin_amdgcn_workgroup_id_x() * kDecodeChunk + wave * (kDecodeChunk / kWaves);
   if (wave_begin > pos) return;
   const int64_t wave_end = wave_begin + kDecodeChunk / kWaves < pos + 1
                                ? wave_begin + kDecodeChunk / kWaves : pos + 1;
 
   QueryRegs<HB> q;
-  load_query<HB>(q, p, row, true, g, c);
+  load_query<HB>(q, p, row, true, g, c, 1.0f);
   const int d = p.idx_dim;
 
   auto load_b = [&](int64_t t0, int kb) {
@@ -229,7 +341,7 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs p) {
     const float ks = my_key < wave_end ? p.k_scale[s.kv0 + my_key] : 0.f;
     float part[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) part[kb] = score_block<HB>(q, cur[kb]);
+    for (int kb = 0; kb < 4; ++kb) part[kb] = score_block<HB, false>(q, cur[kb], 0.f);
     const float v = reduce_four_blocks(part[0], part[1], part[2], part[3]);
     if (my_key < wave_end) p.scores[row * p.ld + my_key] = v * ks;
     if (has_next) {
@@ -243,15 +355,18 @@ template <int HB, int QW>
 hipError_t launch_prefill(const IndexerArgs &a, hipStream_t stream) {
   constexpr int QT = kWaves * QW;
   const int64_t qtiles = (a.seq.max_q_len + QT - 1) / QT;
-  // Key split: as long as possible (fewer Q re-loads) while keeping several
-  // workgroups per CU; the split count is padded to a multiple of 8 so that a
-  // split always lands on the same XCD (workgroups go round-robin over 8 XCDs).
-  int64_t split = 2048;
-  auto blocks = [&](int64_t sp) {
-    const int64_t ns = ((a.seq.max_kv_len + sp - 1) / sp + 7) / 8 * 8;
-    return ns * qtiles * a.seq.batch;
+  // Key split: the longest (256..4096 keys) that still leaves about 6K
+  // workgroups with work, i.e. several rounds of the 256 CUs x 2-3 resident
+  // workgroups, so that the causal tail evens out.  Longer splits re-load the
+  // queries and rebuild their linear operand less often.  Work estimate: the
+  // longest sequence's queries sit at its last max_q_len positions.
+  const double first_pos = (double)(a.seq.max_kv_len - a.seq.max_q_len);
+  auto busy_blocks = [&](int64_t sp) {
+    const double t = (double)qtiles;
+    return ((t * first_pos + QT * t * (t + 1) / 2) / sp + t / 2) * a.seq.batch;
   };
-  while (split > kKeyTile && blocks(split) < 4 * 256) split /= 2;
+  int64_t split = 4096;
+  while (split > 256 && busy_blocks(split) < 6144) split /= 2;
   const int64_t nsplit = ((a.seq.max_kv_len + split - 1) / split + 7) / 8 * 8;
   dim3 grid((unsigned)nsplit, (unsigned)qtiles, (unsigned)a.seq.batch);
   hipLaunchKernelGGL((indexer_prefill_kernel<HB, QW>), grid, dim3(256), 0, stream, a, (int)split);
@@ -269,7 +384,7 @@ template <int HB>
 hipError_t dispatch(const IndexerArgs &a, hipStream_t stream) {
   // A handful of query rows per sequence: stream keys per row.
   if (a.seq.max_q_len <= 2) return launch_decode<HB>(a, stream);
-  return launch_prefill<HB, (HB >= 4 ? 8 / HB : 4)>(a, stream);
+  return launch_prefill<HB, (HB >= 8 ? 1 : (HB >= 2 ? 2 : 4))>(a, stream);
 }
 
 }  // namespace

@@ -71,7 +71,7 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int lane) {
 
 // Exclusive scan over the workgroup in thread order; also returns the total.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, TopkShared &sh, uint32_t &total) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63, wave = tid >> 6;
   const uint32_t inc = wave_inclusive_scan(v, lane);
   if (lane == 63) sh.scan[wave] = inc;
   __syncthreads();
@@ -89,7 +89,7 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, TopkShared 
 }
 
 __device__ __forceinline__ uint32_t block_or(uint32_t v, TopkShared &sh, bool is_and) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63, wave = tid >> 6;
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) {
     const uint32_t t = __shfl_xor(v, d, 64);
@@ -109,7 +109,7 @@ __device__ __forceinline__ uint32_t block_or(uint32_t v, TopkShared &sh, bool is
 template <typename Get>
 __device__ void radix_select(Get get, int64_t count, uint32_t kth, TopkShared &sh, uint32_t &thr,
                              uint32_t &n_above) {
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63;
   uint32_t vor = 0u, vand = 0xFFFFFFFFu;
   for (int64_t i = tid; i < count; i += kThreads) {
     const uint32_t k = get(i);
@@ -180,7 +180,7 @@ __device__ void radix_select(Get get, int64_t count, uint32_t kth, TopkShared &s
 
 // Emit rows with n <= k: positions 0..n-1, then -1.
 __device__ void emit_all(int32_t *out, int64_t n, int k) {
-  for (int i = threadIdx.x; i < k; i += kThreads) out[i] = i < n ? i : -1;
+  for (int i = (int)__builtin_amdgcn_workitem_id_x(); i < k; i += kThreads) out[i] = i < n ? i : -1;
 }
 
 // Exact fallback over the row in global memory.
@@ -195,7 +195,7 @@ __device__ void select_from_global(const float *row, int64_t n, int k, int32_t *
     uint32_t n_eq = 0;
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-      const int64_t i = base + (int64_t)threadIdx.x * V + e;
+      const int64_t i = base + (int64_t)__builtin_amdgcn_workitem_id_x() * V + e;
       key[e] = i < n ? order_key(row[i]) : 0u;
       n_eq += (i < n && key[e] == thr) ? 1u : 0u;
     }
@@ -205,7 +205,7 @@ __device__ void select_from_global(const float *row, int64_t n, int k, int32_t *
     uint32_t n_take = 0;
 #pragma unroll
     for (int e = 0; e < V; ++e) {
-      const int64_t i = base + (int64_t)threadIdx.x * V + e;
+      const int64_t i = base + (int64_t)__builtin_amdgcn_workitem_id_x() * V + e;
       bool t = false;
       if (i < n) {
         if (key[e] > thr) t = true;
@@ -218,7 +218,7 @@ __device__ void select_from_global(const float *row, int64_t n, int k, int32_t *
     uint32_t at = written + block_exclusive_scan(n_take, sh, tk_total);
 #pragma unroll
     for (int e = 0; e < V; ++e)
-      if (take[e]) out[at++] = (int32_t)(base + (int64_t)threadIdx.x * V + e);
+      if (take[e]) out[at++] = (int32_t)(base + (int64_t)__builtin_amdgcn_workitem_id_x() * V + e);
     eq_seen += eq_total;
     written += tk_total;
   }
@@ -227,7 +227,7 @@ __device__ void select_from_global(const float *row, int64_t n, int k, int32_t *
 __global__ __launch_bounds__(kThreads)
 void topk_kernel(TopkArgs p) {
   __shared__ TopkShared sh;
-  const int64_t row = blockIdx.x;
+  const int64_t row = __builtin_amdgcn_workgroup_id_x();
   const int b = find_seq(p.seq, row);
   const SeqInfo s = load_seq(p.seq, b);
   int32_t *out = p.idx + row * p.k;
@@ -246,7 +246,7 @@ void topk_kernel(TopkArgs p) {
     select_from_global(rowp, n, k, out, sh);
     return;
   }
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63;
 
   // 2. lower bound on the k-th key from a sample (all keys if the row fits)
   uint32_t t_lo = 0u;
