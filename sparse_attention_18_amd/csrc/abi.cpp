@@ -147,6 +147,7 @@ dsa::AttnArgs attn_args(const dsa_problem *p, const uint16_t *q, const uint16_t 
   a.scale = p->softmax_scale;
   a.workspace = ws;
   a.workspace_bytes = wsb;
+  a.nsplit = 1;
   return a;
 }
 

@@ -48,6 +48,7 @@ struct AttnArgs {
   float scale;
   void *workspace;
   size_t workspace_bytes;
+  int32_t nsplit;    // workgroups per token (set by the launcher)
 };
 
 hipError_t launch_indexer(const IndexerArgs &a, hipStream_t stream);
@@ -92,14 +93,22 @@ __device__ __forceinline__ int64_t row_pos(const SeqInfo &s, int64_t r) {
   return p > s.kvlen - 1 ? s.kvlen - 1 : p;
 }
 
-// Sequence owning packed query row r (binary search over q_offsets).
+// Sequence owning packed query row r: the last b with q_offsets[b] <= r
+// (offsets are non-decreasing, so that is the count of such b, minus one).
+// r must be uniform across the wave and every lane active: each lane loads
+// offsets lane, lane + 64, ... at once and a ballot counts them, which costs
+// one memory round trip instead of the log2(batch) dependent loads of a
+// binary search.
 __device__ __forceinline__ int find_seq(const SeqLayout &L, int64_t r) {
-  int lo = 0, hi = L.batch - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if ((int64_t)L.q_offsets[mid] <= r) lo = mid; else hi = mid - 1;
+  const int lane = __lane_id();
+  int cnt = 0;
+#pragma unroll 4
+  for (int base = 0; base < L.batch; base += 64) {
+    const int i = base + lane;
+    const bool le = i < L.batch && (int64_t)L.q_offsets[i] <= r;
+    cnt += __popcll(__ballot(le));
   }
-  return lo;
+  return cnt > 0 ? cnt - 1 : 0;
 }
 
 }  // namespace dsa

@@ -32,6 +32,13 @@
 //    heads.  V^T comes from the row-major tile through ds_read_b64_tr_b16,
 //    whose rate is well below ds_read_b128 -- with the dims split each V
 //    element is read through it once per workgroup rather than once per wave.
+//
+// Few tokens (decode): the token's compacted index list is cut into nsplit
+// contiguous ranges, one workgroup each, so that the batch fills the chip.
+// Each range's workgroup writes its unnormalised O, its exponent frame and its
+// softmax denominator per head to the workspace; a small combine kernel then
+// rescales the ranges to their common maximum frame (the usual merge of
+// partial softmax sums) and writes out and lse.
 #include "common.h"
 #include "launch.h"
 
@@ -104,12 +111,31 @@ void mla_sparse_attn_kernel(AttnArgs p) {
 
   // Raw ids: this kernel is large enough that the ockl wrappers behind
   // blockIdx/threadIdx are not reliably inlined.
-  const int64_t t = __builtin_amdgcn_workgroup_id_x();
-  const int b = find_seq(p.seq, t);
-  const SeqInfo s = load_seq(p.seq, b);
+  // Workgroup id = split * total_q + token: when total_q is a multiple of 8
+  // the splits of a token share an XCD (ids go round-robin over the 8 XCDs),
+  // so its Q rows are read once into that XCD's L2.
+  const int64_t wg = __builtin_amdgcn_workgroup_id_x();
+  const int split = (int)(wg / p.seq.total_q);
+  const int64_t t = wg - (int64_t)split * p.seq.total_q;
   const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63, wave = tid >> 6;
   const int G = lane >> 5, c32 = lane & 31, jl = lane & 15, half = (lane >> 4) & 1;
   const int k = p.k;
+
+  // Q^T operands of this wave's heads: k-step kk = dims 16kk..16kk+15, lane
+  // (G, c32) holds head 32*wave + c32, dims 16kk + 8G .. +7.  Row t < total_q
+  // is always in bounds.  Issued first: they depend on t only, so their
+  // latency overlaps the sequence lookup and the index compaction.
+  const int head = wave * 32 + c32;
+  v8bf qb[kD / 16];
+  {
+    const uint16_t *qrow = p.q + (t * H + head) * (int64_t)kD + 8 * G;
+#pragma unroll
+    for (int kk = 0; kk < kD / 16; ++kk)
+      qb[kk] = as_v8bf(*reinterpret_cast<const v4i *>(qrow + 16 * kk));
+  }
+
+  const int b = find_seq(p.seq, t);
+  const SeqInfo s = load_seq(p.seq, b);
   const bool row_ok = t >= s.q0 && t < s.q1;
 
   // Compact the row's valid indices (in order) into idxl; m = their count.
@@ -150,18 +176,13 @@ void mla_sparse_attn_kernel(AttnArgs p) {
       if (vals[e] >= 0) idxl[base++] = vals[e];
     __syncthreads();
   }
-  // Q^T operands of this wave's heads: k-step kk = dims 16kk..16kk+15, lane
-  // (G, c32) holds head 32*wave + c32, dims 16kk + 8G .. +7.  Row t < total_q
-  // is always in bounds.
-  const int head = wave * 32 + c32;
-  v8bf qb[kD / 16];
-  {
-    const uint16_t *qrow = p.q + (t * H + head) * (int64_t)kD + 8 * G;
-#pragma unroll
-    for (int kk = 0; kk < kD / 16; ++kk)
-      qb[kk] = as_v8bf(*reinterpret_cast<const v4i *>(qrow + 16 * kk));
-  }
-  const int ntiles = (m + kBN - 1) / kBN;
+  // This workgroup's range of the compacted list: whole tiles, split evenly.
+  const int chunk = (((m + p.nsplit - 1) / p.nsplit) + kBN - 1) / kBN * kBN;
+  const int r_begin = split * chunk < m ? split * chunk : m;
+  const int r_end = r_begin + chunk < m ? r_begin + chunk : m;
+  const int nrows = r_end - r_begin;
+  const int ntiles = (nrows + kBN - 1) / kBN;
+  const int *idxr = idxl + r_begin;
   wait_vmcnt<0>();   // Q^T operands resident before any LDS-DMA is in flight
 
   // Gather of tile `tl` into its stage buffer; rows past m repeat a valid
@@ -177,7 +198,7 @@ void mla_sparse_attn_kernel(AttnArgs p) {
     for (int q = 0; q < kRB; ++q) {
       const int row = 8 * (wave + NW * q) + (lane >> 3);
       const int r = tl * kBN + row;
-      const int gi = idxl[r < m ? r : 0];
+      const int gi = idxr[r < nrows ? r : 0];
       src[q] = kvseq + (uint32_t)gi * (uint32_t)(kD * 2) + 16 * ((lane & 7) ^ ((row >> 1) & 7));
     }
     return (uint32_t)(uintptr_t)(DSA_LDS uint8_t *)kvbuf[tl % kStages];
@@ -250,7 +271,7 @@ void mla_sparse_attn_kernel(AttnArgs p) {
     // ---- softmax of tile tq: scale + mask + max, frame update, exp2 + sum
     // + bf16, publish P^T into pbuf[tq & 1].
     auto sm_scale = [&](v16f &sc, int tq, int j0, int j1, float &mt) {
-      const int valid_rows = m - tq * kBN;   // >= 1
+      const int valid_rows = nrows - tq * kBN;   // >= 1
       const bool partial = valid_rows < kBN; // only the last tile can be partial
 #pragma unroll
       for (int jj = j0; jj < j1; ++jj) {
@@ -344,8 +365,29 @@ void mla_sparse_attn_kernel(AttnArgs p) {
     if (tid == 0) s_flag = 0;
   }
 
-  // ---- epilogue: denominators through LDS, normalise, store bf16
   const float l_tot = sum_across_halves(l_part);
+  if (p.nsplit > 1) {
+    // ---- partial epilogue: unnormalised O^T, frame and denominator per head
+    if (!row_ok) return;
+    const int64_t slot = (int64_t)split * p.seq.total_q + t;
+    float *wo = reinterpret_cast<float *>(p.workspace) + slot * H * (int64_t)kDL;
+    float2 *wml = reinterpret_cast<float2 *>(reinterpret_cast<float *>(p.workspace) +
+                                             (int64_t)p.nsplit * p.seq.total_q * H * kDL);
+    if (G == 0) wml[slot * H + head] = make_float2(m_used, l_tot);
+#pragma unroll
+    for (int nb = 0; nb < NW; ++nb) {
+      float *ohead = wo + (nb * 32 + c32) * (int64_t)kDL + wave * DW + 4 * G;
+#pragma unroll
+      for (int u = 0; u < MB; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<v4f *>(ohead + 32 * u + 8 * i) =
+              v4f{o[u][nb][4 * i], o[u][nb][4 * i + 1], o[u][nb][4 * i + 2], o[u][nb][4 * i + 3]};
+    }
+    return;
+  }
+
+  // ---- epilogue: denominators through LDS, normalise, store bf16
   if (G == 0) lsum[head] = l_tot;
   if (p.lse != nullptr && G == 0 && row_ok)
     p.lse[t * H + head] = l_tot > 0.f ? (m_used + log2f(l_tot)) * kLn2 : -INFINITY;
@@ -366,6 +408,43 @@ void mla_sparse_attn_kernel(AttnArgs p) {
         *reinterpret_cast<v2i *>(ohead + 32 * u + 8 * i) = v2i{(int)w0, (int)w1};
       }
   }
+}
+
+// Merge of the nsplit partial results of a token (MFMA path, nsplit > 1):
+// with frames m_s (log2 units), denominators l_s and unnormalised O_s,
+//   M = max_s m_s,  e_s = 2^(m_s - M),  out = sum_s e_s O_s / sum_s e_s l_s,
+//   lse = (M + log2 sum_s e_s l_s) * ln 2.
+// One workgroup of 128 threads per (token, head); thread i owns dims 4i..4i+3.
+__global__ __launch_bounds__(128) void combine_splits_kernel(AttnArgs p, int heads) {
+  const int64_t th = __builtin_amdgcn_workgroup_id_x();     // token * heads + head
+  const int tid = (int)__builtin_amdgcn_workitem_id_x();
+  const int64_t t = th / heads;
+  const int b = find_seq(p.seq, t);
+  const SeqInfo s = load_seq(p.seq, b);
+  if (t < s.q0 || t >= s.q1) return;
+  const int S = p.nsplit;
+  const int64_t per_split = p.seq.total_q * heads;
+  const float *wo = reinterpret_cast<const float *>(p.workspace);
+  const float2 *wml = reinterpret_cast<const float2 *>(wo + (int64_t)S * per_split * kDL);
+  float M = -INFINITY;
+  for (int sp = 0; sp < S; ++sp) M = fmaxf(M, wml[sp * per_split + th].x);
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  if (M != -INFINITY) {
+    for (int sp = 0; sp < S; ++sp) {
+      const float2 ml = wml[sp * per_split + th];
+      if (ml.x == -INFINITY) continue;
+      const float e = __builtin_amdgcn_exp2f(ml.x - M);
+      L = fmaf(e, ml.y, L);
+      const v4f x = *reinterpret_cast<const v4f *>(wo + (sp * per_split + th) * kDL + 4 * tid);
+      acc = acc + e * x;
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  const uint32_t w0 = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  const uint32_t w1 = pack_bf16x2(acc[2] * inv, acc[3] * inv);
+  *reinterpret_cast<v2i *>(p.out + th * kDL + 4 * tid) = v2i{(int)w0, (int)w1};
+  if (tid == 0 && p.lse != nullptr) p.lse[th] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 // Small-shape path: any H <= 128 and D <= 1024.  One workgroup per token;
@@ -436,22 +515,43 @@ __global__ __launch_bounds__(kSmallThreads) void small_sparse_attn_kernel(AttnAr
   }
 }
 
+bool mfma_shape(const AttnArgs &a) {
+  // The latent dims split evenly over NW waves only for NW in {1, 2, 4}.
+  return a.d_latent == kDL && a.d_rope == kD - kDL &&
+         (a.heads == 32 || a.heads == 64 || a.heads == 128);
+}
+
+// Workgroups per token: enough that a small batch still covers the 256 CUs.
+int attn_splits(const AttnArgs &a) {
+  if (!mfma_shape(a) || a.seq.total_q == 0) return 1;
+  const int64_t s = 256 / a.seq.total_q;
+  return s >= 4 ? 4 : (s >= 2 ? 2 : 1);
+}
+
 }  // namespace
 
-size_t sparse_attn_workspace_bytes(const AttnArgs &) { return 0; }
+size_t sparse_attn_workspace_bytes(const AttnArgs &a) {
+  const int S = attn_splits(a);
+  if (S == 1) return 0;
+  return (size_t)S * a.seq.total_q * a.heads * (kDL * sizeof(float) + 2 * sizeof(float));
+}
 
-hipError_t launch_sparse_attn(const AttnArgs &a, hipStream_t stream) {
-  if (a.seq.total_q == 0) return hipSuccess;
-  const dim3 grid((unsigned)a.seq.total_q);
-  // The latent dims split evenly over NW waves only for NW in {1, 2, 4}.
-  const bool mfma = a.d_latent == kDL && a.d_rope == kD - kDL &&
-                    (a.heads == 32 || a.heads == 64 || a.heads == 128);
-  if (mfma) {
+hipError_t launch_sparse_attn(const AttnArgs &args, hipStream_t stream) {
+  if (args.seq.total_q == 0) return hipSuccess;
+  AttnArgs a = args;
+  a.nsplit = attn_splits(a);
+  if (a.nsplit > 1 && (a.workspace == nullptr || a.workspace_bytes < sparse_attn_workspace_bytes(a)))
+    return hipErrorInvalidValue;   // the ABI layer checks the size first
+  const dim3 grid((unsigned)(a.seq.total_q * a.nsplit));
+  if (mfma_shape(a)) {
     switch (a.heads / 32) {
       case 1: hipLaunchKernelGGL(mla_sparse_attn_kernel<1>, grid, dim3(64), 0, stream, a); break;
       case 2: hipLaunchKernelGGL(mla_sparse_attn_kernel<2>, grid, dim3(128), 0, stream, a); break;
       default: hipLaunchKernelGGL(mla_sparse_attn_kernel<4>, grid, dim3(256), 0, stream, a); break;
     }
+    if (a.nsplit > 1)
+      hipLaunchKernelGGL(combine_splits_kernel, dim3((unsigned)(a.seq.total_q * a.heads)), dim3(128), 0,
+                         stream, a, (int)a.heads);
   } else {
     hipLaunchKernelGGL(small_sparse_attn_kernel, grid, dim3(kSmallThreads), 0, stream, a);
   }

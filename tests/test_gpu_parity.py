@@ -148,17 +148,26 @@ def _attn_case(H_, dl, dr, T, S, k, seed, fill=None, scale=None, qmul=1.0):
     return q, kv, idx, scale
 
 
-def _run_attn(q, kv, idx, scale, dl, dr):
+def _run_attn(q, kv, idx, scale, dl, dr, pad_to=None):
+    """Attention through the C ABI.  With `pad_to`, extra tokens with no valid
+    index are appended so that the batch is large enough to run one workgroup
+    per token; small batches split every token over several workgroups."""
     T, H_, _ = q.shape
     S = kv.shape[0]
     k = idx.shape[1]
-    prob = dsa.Problem(q_offsets=[0, T], kv_offsets=[0, S], q_pos0=[S - T], idx_heads=4,
+    if pad_to is not None and pad_to > T:
+        q = torch.cat([q, torch.zeros(pad_to - T, H_, q.shape[2], dtype=q.dtype)])
+        idx = torch.cat([idx, torch.full((pad_to - T, k), -1, dtype=idx.dtype)])
+    Tp = q.shape[0]
+    prob = dsa.Problem(q_offsets=[0, Tp], kv_offsets=[0, S], q_pos0=[max(S - Tp, 0)], idx_heads=4,
                        idx_dim=32, heads=H_, d_latent=dl, d_rope=dr, topk=k, softmax_scale=scale)
-    out = torch.full((T, H_, dl), float("nan"), dtype=torch.bfloat16, device="cuda")
-    lse = torch.full((T, H_), float("nan"), dtype=torch.float32, device="cuda")
-    dsa.sparse_attn(prob, q.cuda(), kv.cuda(), idx.cuda(), out, lse)
+    out = torch.full((Tp, H_, dl), float("nan"), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((Tp, H_), float("nan"), dtype=torch.float32, device="cuda")
+    nws = dsa.workspace_bytes(prob, dsa.WS_ATTN)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda") if nws else None
+    dsa.sparse_attn(prob, q.cuda(), kv.cuda(), idx.cuda(), out, lse, workspace=ws)
     torch.cuda.synchronize()
-    return out, lse
+    return out[:T], lse[:T]
 
 
 @pytest.mark.parametrize("H_", [128, 64, 32, 96])
@@ -168,11 +177,12 @@ def test_attention_mla_shape_with_padding(H_):
     fills = [2048, 2048, 1, 5, 31, 32, 33, 100, 1000, 2047, 0, 64] * 2
     q, kv, idx, scale = _attn_case(H_, 512, 64, T, S, k, seed=H_, fill=lambda t: fills[t],
                                    scale=1 / math.sqrt(192))
-    out, lse = _run_attn(q, kv, idx, scale, 512, 64)
     rows = [t for t in range(T) if fills[t] > 0]
-    H.check_attention_rows(out, lse, q, kv, idx, rows, [0] * len(rows), scale, 512)
     empty = [t for t in range(T) if fills[t] == 0]
-    assert (out[empty].float() == 0).all() and torch.isinf(lse[empty]).all()
+    for pad_to in (None, 264):        # split over workgroups, then one workgroup per token
+        out, lse = _run_attn(q, kv, idx, scale, 512, 64, pad_to=pad_to)
+        H.check_attention_rows(out, lse, q, kv, idx, rows, [0] * len(rows), scale, 512)
+        assert (out[empty].float() == 0).all() and torch.isinf(lse[empty]).all()
 
 
 def test_attention_indices_with_holes_and_out_of_range():
@@ -202,8 +212,9 @@ def test_attention_frame_overflow_recompute():
     q, kv = q.to(torch.bfloat16), kv.to(torch.bfloat16)
     idx = torch.arange(k, dtype=torch.int32).repeat(T, 1) + 200   # rows 200..455, 400 late
     scale = 1 / math.sqrt(192)
-    out, lse = _run_attn(q, kv, idx, scale, 512, 64)
-    H.check_attention_rows(out, lse, q, kv, idx, list(range(T)), [0] * T, scale, 512)
+    for pad_to in (None, 264):
+        out, lse = _run_attn(q, kv, idx, scale, 512, 64, pad_to=pad_to)
+        H.check_attention_rows(out, lse, q, kv, idx, list(range(T)), [0] * T, scale, 512)
 
 
 @pytest.mark.parametrize("shape", [(8, 64, 16), (16, 128, 32), (128, 512, 64)])
