@@ -13,12 +13,15 @@
 //  * the token's valid indices are compacted once into LDS; its selected
 //    rows are then gathered 32 at a time straight into LDS with LDS-DMA loads
 //    (global_load_lds, 16-byte chunks), three tiles in flight; every head of
-//    the token shares this one gather.  A tile is stored chunk-group major:
-//    16-byte chunk c of row r sits at slot ((c / 8) * 32 + r) * 8 +
-//    ((c % 8) ^ ((r >> 1) & 7)).  One 1 KB DMA load then covers 8 rows x 8
-//    chunks of one group, so a wave's loads need one row index per tile and
-//    immediate offsets, and the MFMA operand reads of 16 consecutive rows hit
-//    16 distinct bank groups;
+//    the token shares this one gather.  A tile is a sequence of 1 KB blocks,
+//    row-block major: block (r / 8) * 9 + c / 8 holds chunks 8(c/8)..+7 of
+//    rows 8(r/8)..+7, and 16-byte chunk c of row r sits in it at slot
+//    (r % 8) * 8 + ((c % 8) ^ ((r >> 1) & 7)).  One DMA load fills one block,
+//    so a wave's loads need one row index per tile and immediate offsets; a
+//    wave's 9 blocks of a row block are consecutive, so one M0 value serves
+//    four loads (the instruction offset moves the LDS destination and the
+//    global source alike).  MFMA operand reads of 16 consecutive rows hit 16
+//    distinct bank groups;
 //  * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16: wave w takes heads
 //    32w..32w+31 (N), Q^T resident in registers, the 32 keys of the tile as
 //    M and the 576 dims as K;
@@ -53,7 +56,9 @@ constexpr int kPitch = kChunks * 16;         // 1152 B
 constexpr int kTileBytes = kBN * kPitch;     // 36864 B
 constexpr int kTileInsts = kBN * kChunks / 64;  // 36 wave-wide 1 KB loads per tile
 constexpr int kStages = 3;
-constexpr int kGroupBytes = kBN * 8 * 16;      // one 8-chunk group of a tile
+constexpr int kGroups = kChunks / 8;           // 9 chunk groups per row
+constexpr int kBlock = 1024;                   // 8 rows x 8 chunks: one DMA load
+constexpr int kRowBlockBytes = kGroups * kBlock;   // 8 rows x 72 chunks
 constexpr int kMaxK = 4096;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -64,24 +69,51 @@ __device__ __forceinline__ v8bf as_v8bf(const v4i &x) { return __builtin_bit_cas
 
 // Byte offset, inside a tile, of 16-byte chunk c of row r (see the layout note).
 __device__ __forceinline__ int tile_off(int r, int c) {
-  return (((c >> 3) * kBN + r) * 8 + ((c ^ (r >> 1)) & 7)) * 16;
+  return ((r >> 3) * kGroups + (c >> 3)) * kBlock + ((r & 7) * 8 + ((c ^ (r >> 1)) & 7)) * 16;
 }
 
-// One LDS-DMA load: 16 bytes from `g` (per lane) to LDS at lds_base + 16 * lane.
-// Issued from inline assembly so that the compiler does not tie later LDS
-// reads of other tile buffers to its completion; the kernel waits for it
-// explicitly (vmcnt) before the barrier that publishes the tile.  M0 is
-// saved and restored around the load.
-__device__ __forceinline__ void lds_dma16(const void *g, uint32_t lds_base) {
+// LDS-DMA loads in scalar-base form: lane i's 16 bytes come from
+// base + voff(i) + offset and land at M0 + offset + 16 i.  Four loads share
+// one M0 value and fill the consecutive 1 KB blocks M0 + 1024 k (offset
+// 1024 k); the instruction offset moves the global address as well, so
+// base k is passed already shifted by -1024 k.  The bases are uniform
+// (SGPR pairs); the per-lane part is one 32-bit offset.
+// A uniform pointer as an SGPR-pair value.  readfirstlane returns a signed
+// int: both halves go through uint32_t so that neither is sign-extended.
+__device__ __forceinline__ uint64_t sbase(const void *p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (uint64_t)lo | ((uint64_t)hi << 32);
+}
+
+__device__ __forceinline__ void lds_dma16_x4(uint32_t voff, uint64_t b0, uint64_t b1, uint64_t b2,
+                                             uint64_t b3, uint32_t lds_base) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
+      "s_mov_b32 m0, %6\n\t"
       "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "global_load_lds_dwordx4 %1, %3 offset:1024\n\t"
+      "global_load_lds_dwordx4 %1, %4 offset:2048\n\t"
+      "global_load_lds_dwordx4 %1, %5 offset:3072\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "v"(g), "s"(lds_base)
+      : "v"(voff), "s"(b0), "s"(b1), "s"(b2), "s"(b3), "s"(lds_base)
+      : "memory");
+}
+
+__device__ __forceinline__ void lds_dma16_x1(uint32_t voff, uint64_t b0, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(b0), "s"(lds_base)
       : "memory");
 }
 
@@ -99,7 +131,6 @@ void mla_sparse_attn_kernel(AttnArgs p) {
   constexpr int T = NW * 64;                 // threads
   constexpr int DW = kDL / NW;               // latent dims per wave in P.V
   constexpr int MB = DW / 32;                // 32-dim M blocks per wave
-  constexpr int kDmaPerWave = kTileInsts / NW;
   static_assert(DW * NW == kDL && MB * 32 == DW, "latent dims must split evenly over waves");
   static_assert(kTileInsts % NW == 0, "tile loads must split evenly over waves");
   __shared__ __attribute__((aligned(16))) uint8_t kvbuf[kStages][kTileBytes];
@@ -117,7 +148,10 @@ void mla_sparse_attn_kernel(AttnArgs p) {
   const int64_t wg = __builtin_amdgcn_workgroup_id_x();
   const int split = (int)(wg / p.seq.total_q);
   const int64_t t = wg - (int64_t)split * p.seq.total_q;
-  const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63, wave = tid >> 6;
+  // The wave index is uniform: readfirstlane keeps everything derived from
+  // it (LDS block bases, M0 values) in scalar registers.
+  const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = lane >> 5, c32 = lane & 31, jl = lane & 15, half = (lane >> 4) & 1;
   const int k = p.k;
 
@@ -186,27 +220,35 @@ void mla_sparse_attn_kernel(AttnArgs p) {
   wait_vmcnt<0>();   // Q^T operands resident before any LDS-DMA is in flight
 
   // Gather of tile `tl` into its stage buffer; rows past m repeat a valid
-  // row.  Load i covers chunk group i/4 of rows 8*(i%4) .. +7: lane (row
-  // 8*(i%4) + lane/8, slot lane%8) receives logical chunk 8*(i/4) +
-  // ((lane%8) ^ f(row)).  This wave owns row blocks rb = wave + NW*q; its
-  // load d (< kDmaPerWave) is row block q = d / 9, chunk group d % 9.
+  // row.  This wave owns row blocks rb = wave + NW*q (q < kRB); the load of
+  // chunk group cg of row block rb fills block rb*9 + cg: lane (row 8rb +
+  // lane/8, slot lane%8) receives logical chunk 8cg + ((lane%8) ^ f(row)).
+  // A row block's 9 loads go out as three windows (groups 0-3, 4-7, 8), one
+  // M0 value each.
   constexpr int kRB = 4 / NW;
-  constexpr int kGroups = kChunks / 8;
+  constexpr int kWindows = 3 * kRB;
+  // Uniform sequence base; a row's byte offset fits in 32 bits (the host
+  // bounds max_kv_len * 1152 below 2^32 for this path).
   const uint8_t *kvseq = reinterpret_cast<const uint8_t *>(p.kv + s.kv0 * (int64_t)kD);
-  auto gather_setup = [&](int tl, const uint8_t *(&src)[kRB]) {
+  auto gather_setup = [&](int tl, uint32_t (&voff)[kRB]) {
 #pragma unroll
     for (int q = 0; q < kRB; ++q) {
       const int row = 8 * (wave + NW * q) + (lane >> 3);
       const int r = tl * kBN + row;
       const int gi = idxr[r < nrows ? r : 0];
-      src[q] = kvseq + (uint32_t)gi * (uint32_t)(kD * 2) + 16 * ((lane & 7) ^ ((row >> 1) & 7));
+      voff[q] = (uint32_t)gi * (uint32_t)(kD * 2) + 16 * ((lane & 7) ^ ((row >> 1) & 7));
     }
-    return (uint32_t)(uintptr_t)(DSA_LDS uint8_t *)kvbuf[tl % kStages];
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(DSA_LDS uint8_t *)kvbuf[tl % kStages]);
   };
-  auto gather_one = [&](const uint8_t *const (&src)[kRB], uint32_t base, int d) {
-    const int q = d / kGroups, cg = d % kGroups;
-    lds_dma16(src[q] + 128 * cg,
-              __builtin_amdgcn_readfirstlane(base + (cg * 4 + wave + NW * q) * 1024));
+  // Window w: row block wave + NW*(w/3), chunk groups 4*(w%3) .. (+3, or 8).
+  auto gather_window = [&](const uint32_t (&voff)[kRB], uint32_t base, int w) {
+    const int q = w / 3, win = w % 3;
+    const uint32_t lb = __builtin_amdgcn_readfirstlane(base + ((wave + NW * q) * kGroups + 4 * win) * kBlock);
+    const uint8_t *g = kvseq + 128 * 4 * win;      // chunk group 4*win
+    if (win < 2)
+      lds_dma16_x4(voff[q], sbase(g), sbase(g + 128 - 1024), sbase(g + 256 - 2048), sbase(g + 384 - 3072), lb);
+    else
+      lds_dma16_x1(voff[q], sbase(g), lb);
   };
 
   const float sl2 = p.scale * kLog2e;
@@ -221,11 +263,14 @@ void mla_sparse_attn_kernel(AttnArgs p) {
   // 4G + jl/4 and r0 + 8, dims wave*DW + 32u + 16*half + 4*(jl%4), i.e. group
   // wave*DW/64 + u/2, in-group index 4(u%2) + 2*half + (jl/2)%2, byte 8*(jl%2).
   const int fq = (c32 >> 1) & 7;
-  auto qk_off = [&](int kk) { return (c32 * 8 + ((2 * (kk & 3) + G) ^ fq)) * 16 + kGroupBytes * (kk >> 2); };
+  auto qk_off = [&](int kk) {
+    return (c32 >> 3) * kRowBlockBytes + ((c32 & 7) * 8 + ((2 * (kk & 3) + G) ^ fq)) * 16 + kBlock * (kk >> 2);
+  };
   auto v_off = [&](int hf, int u, int which) {
     const int r = 16 * hf + 4 * G + (jl >> 2) + 8 * which;
     const int in = (4 * (u & 1) + 2 * half + ((jl >> 1) & 1)) ^ ((r >> 1) & 7);
-    return (wave * DW / 64 + (u >> 1)) * kGroupBytes + (r * 8 + in) * 16 + (jl & 1) * 8;
+    return (r >> 3) * kRowBlockBytes + (wave * DW / 64 + (u >> 1)) * kBlock + ((r & 7) * 8 + in) * 16 +
+           (jl & 1) * 8;
   };
   auto load_v = [&](const DSA_LDS uint8_t *tb, int hf, int u) {
     const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DSA_LDS v4s *)(tb + v_off(hf, u, 0)));
@@ -249,9 +294,8 @@ void mla_sparse_attn_kernel(AttnArgs p) {
     // one load every NW k-steps, in the shadow of the MFMA chain.
     auto qk_phase = [&](int tq, bool gnext) {
       constexpr int KS = kD / 16, LA = 3;
-      static_assert(KS == NW * kDmaPerWave, "one load per NW k-steps");
       const DSA_LDS uint8_t *tbq = (const DSA_LDS uint8_t *)kvbuf[tq % kStages];
-      const uint8_t *src[kRB];
+      uint32_t src[kRB];
       uint32_t gbase = 0;
       if (gnext) gbase = gather_setup(tq + 1, src);
       v16f sc = {};
@@ -262,7 +306,10 @@ void mla_sparse_attn_kernel(AttnArgs p) {
       for (int j = 0; j < KS; ++j) {
         sc = mfma_32x32x16_bf16(as_v8bf(a[j % LA]), qb[j], sc);
         if (j + LA < KS) a[j % LA] = *reinterpret_cast<const DSA_LDS v4i *>(tbq + qk_off(j + LA));
-        if (gnext && j % NW == 0) gather_one(src, gbase, j / NW);
+        if (gnext)
+#pragma unroll
+          for (int w = 0; w < kWindows; ++w)
+            if (j == w * KS / kWindows) gather_window(src, gbase, w);
         __builtin_amdgcn_sched_barrier(0);
       }
       return sc;
@@ -274,12 +321,15 @@ void mla_sparse_attn_kernel(AttnArgs p) {
       const int valid_rows = nrows - tq * kBN;   // >= 1
       const bool partial = valid_rows < kBN; // only the last tile can be partial
 #pragma unroll
-      for (int jj = j0; jj < j1; ++jj) {
-        float x = sc[jj] * sl2;
-        if (partial && 8 * (jj >> 2) + 4 * G + (jj & 3) >= valid_rows) x = -INFINITY;
-        sc[jj] = x;
-        mt = fmaxf(mt, x);
+      for (int jj = j0; jj < j1; ++jj) sc[jj] *= sl2;
+      if (partial) {
+        const int vr = valid_rows - 4 * G;      // element jj is row 8(jj/4) + 4G + jj%4
+#pragma unroll
+        for (int jj = j0; jj < j1; ++jj)
+          if (8 * (jj >> 2) + (jj & 3) >= vr) sc[jj] = -INFINITY;
       }
+#pragma unroll
+      for (int jj = j0; jj < j1; ++jj) mt = fmaxf(mt, sc[jj]);
     };
     auto sm_frame = [&](float mt) {
       mt = max_across_halves(mt);
@@ -332,10 +382,10 @@ void mla_sparse_attn_kernel(AttnArgs p) {
     // step t+1 overwrites.
     if (ntiles > 0) {
       {
-        const uint8_t *src[kRB];
+        uint32_t src[kRB];
         const uint32_t gbase = gather_setup(0, src);
 #pragma unroll
-        for (int d = 0; d < kDmaPerWave; ++d) gather_one(src, gbase, d);
+        for (int w = 0; w < kWindows; ++w) gather_window(src, gbase, w);
       }
       for (int t = 0; t <= ntiles; ++t) {
         // This wave's share of tile t landed (nothing is in flight at the last
