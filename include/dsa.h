@@ -126,10 +126,14 @@ dsa_status dsa_topk(const dsa_problem *p, const float *scores, int64_t ld_scores
  * accumulation, bf16 output rounded to nearest even.
  *   q [total_q, H, D] bf16     kv [total_kv, D] bf16     topk_idx [total_q, k] int32
  *   out [total_q, H, d_latent] bf16                      lse [total_q, H] float (nullable)
- * Supported: (d_latent, d_rope) = (512, 64) with H in {32, 64, 128} (the MFMA
- * path), or any D <= 1024 with H <= 128 (a plain small-shape path, which also
- * serves other head counts of the 576-wide shape).
- * workspace: at least dsa_workspace_bytes(p, DSA_WS_ATTN) bytes.
+ * Supported: (d_latent, d_rope) = (512, 64) with H in {32, 64, 128} and
+ * max_kv_len <= 3728270 (the MFMA path; a sequence's rows are addressed with
+ * 32-bit byte offsets), or any D <= 1024 with H <= 128 (a plain small-shape
+ * path, which also serves other head counts of the 576-wide shape).
+ * workspace: at least dsa_workspace_bytes(p, DSA_WS_ATTN) bytes.  It is zero
+ * for large batches; batches of fewer than 128 tokens split each token's
+ * selected rows over several workgroups and need room for the partial
+ * results (nsplit * total_q * H * 2056 bytes).
  */
 dsa_status dsa_sparse_attn(const dsa_problem *p, const uint16_t *q, const uint16_t *kv,
                            const int32_t *topk_idx, uint16_t *out, float *lse,

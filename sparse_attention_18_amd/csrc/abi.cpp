@@ -77,6 +77,10 @@ dsa_status check_attn_dims(const dsa_problem *p) {
             "d_latent must be >= 1 and d_rope >= 0");
   DSA_CHECK(mfma_attn_shape(p) || p->d_latent + p->d_rope <= 1024, DSA_ERR_UNSUPPORTED,
             "d_latent + d_rope must be <= 1024 outside the (512, 64) MFMA shape");
+  // The MFMA path addresses a sequence's rows with 32-bit byte offsets.
+  DSA_CHECK(!mfma_attn_shape(p) || p->max_kv_len <= (int64_t)(UINT32_MAX / 1152u), DSA_ERR_UNSUPPORTED,
+            "max_kv_len must be <= %u for the (512, 64) attention shape (got %lld)",
+            (unsigned)(UINT32_MAX / 1152u), (long long)p->max_kv_len);
   DSA_CHECK(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f, DSA_ERR_INVALID_ARGUMENT,
             "softmax_scale must be finite and > 0");
   return DSA_OK;

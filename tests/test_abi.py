@@ -96,6 +96,7 @@ def test_indexer_rejects_null_problem_bad_ld_and_pointers():
     (dict(softmax_scale=float("nan")), binding.DSA_ERR_INVALID_ARGUMENT, "softmax_scale"),
     (dict(softmax_scale=0.0), binding.DSA_ERR_INVALID_ARGUMENT, "softmax_scale"),
     (dict(d_latent=0), binding.DSA_ERR_INVALID_ARGUMENT, "d_latent"),
+    (dict(max_kv_len=3728271, total_kv=3728271), binding.DSA_ERR_UNSUPPORTED, "max_kv_len"),
 ])
 def test_attention_rejects_bad_problems(kw, status, needle):
     assert _attn(_problem(**kw)) == status
