@@ -117,6 +117,20 @@ __device__ __forceinline__ void lds_dma16_x1(uint32_t voff, uint64_t b0, uint32_
       : "memory");
 }
 
+// S^T accumulation MFMAs, pinned to VGPRs.  The P.V accumulators fill all
+// 256 AGPRs; left to itself the compiler puts this accumulator in AGPRs too
+// and spills part of O.  The chain's dependent MFMAs are interlocked by the
+// hardware; the VALU reads of the result follow qk_drain().
+__device__ __forceinline__ void qk_mfma_first(v16f &acc, const v4i &a, const v8bf &b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void qk_mfma(v16f &acc, const v4i &a, const v8bf &b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+// Wait states between the last S^T MFMA (written through asm, so invisible
+// to the compiler's hazard tracking) and the first VALU read of its result.
+__device__ __forceinline__ void qk_drain() { asm volatile("s_nop 15\n\ts_nop 15" ::: "memory"); }
+
 // s_waitcnt on vmcnt only (expcnt and lgkmcnt left at their maxima).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -290,28 +304,47 @@ void mla_sparse_attn_kernel(AttnArgs p) {
     l_part = 0.f;
     bool overflow = false;
 
-    // ---- S^T of tile `tq`; the next tile's gather (when `gnext`) is issued
-    // one load every NW k-steps, in the shadow of the MFMA chain.
-    auto qk_phase = [&](int tq, bool gnext) {
-      constexpr int KS = kD / 16, LA = 3;
+    // ---- one pipeline step: S^T of tile `tq` interleaved with
+    // O^T[dims of this wave][all heads] += V^T . P^T of the previous tile
+    // (tile buffer tbp, P^T buffer pbp).  The two are independent, so
+    // alternating their MFMAs hides the dependent-issue latency of the S^T
+    // accumulation chain.  The next tile's gather (when `gnext`) goes out in
+    // a few windows along the way.
+    auto step_phase = [&](int tq, const DSA_LDS uint8_t *tbp, const DSA_LDS uint8_t *pbp, bool gnext) {
+      constexpr int KS = kD / 16, LA = 3, NPV = 2 * MB * NW;
+      static_assert(NPV <= KS, "P.V MFMAs ride along the S^T chain");
       const DSA_LDS uint8_t *tbq = (const DSA_LDS uint8_t *)kvbuf[tq % kStages];
       uint32_t src[kRB];
       uint32_t gbase = 0;
       if (gnext) gbase = gather_setup(tq + 1, src);
-      v16f sc = {};
+      v16f sc;
       v4i a[LA];
 #pragma unroll
       for (int kk = 0; kk < LA; ++kk) a[kk] = *reinterpret_cast<const DSA_LDS v4i *>(tbq + qk_off(kk));
+      // P.V MFMA i: group g = i / NW = hf * MB + u, head block nb = i % NW.
+      v8bf pbn[NW], av[2];
 #pragma unroll
-      for (int j = 0; j < KS; ++j) {
-        sc = mfma_32x32x16_bf16(as_v8bf(a[j % LA]), qb[j], sc);
-        if (j + LA < KS) a[j % LA] = *reinterpret_cast<const DSA_LDS v4i *>(tbq + qk_off(j + LA));
+      for (int nb = 0; nb < NW; ++nb) pbn[nb] = load_p(pbp, 0, nb);
+      av[0] = load_v(tbp, 0, 0);
+#pragma unroll
+      for (int i = 0; i < KS; ++i) {
+        if (i == 0) qk_mfma_first(sc, a[0], qb[0]);
+        else qk_mfma(sc, a[i % LA], qb[i]);
+        if (i + LA < KS) a[i % LA] = *reinterpret_cast<const DSA_LDS v4i *>(tbq + qk_off(i + LA));
+        if (i < NPV) {
+          const int g = i / NW, nb = i % NW, hf = g / MB, u = g % MB;
+          if (nb == 0 && g + 1 < 2 * MB) av[(g + 1) & 1] = load_v(tbp, (g + 1) / MB, (g + 1) % MB);
+          o[u][nb] = mfma_32x32x16_bf16(av[g & 1], pbn[nb], o[u][nb]);
+          // last use of this head block's P^T for hf = 0: fetch the hf = 1 one
+          if (hf == 0 && u == MB - 1) pbn[nb] = load_p(pbp, 1, nb);
+        }
         if (gnext)
 #pragma unroll
           for (int w = 0; w < kWindows; ++w)
-            if (j == w * KS / kWindows) gather_window(src, gbase, w);
+            if (i == w * KS / kWindows) gather_window(src, gbase, w);
         __builtin_amdgcn_sched_barrier(0);
       }
+      qk_drain();
       return sc;
     };
 
@@ -354,32 +387,19 @@ void mla_sparse_attn_kernel(AttnArgs p) {
         *reinterpret_cast<v8bf *>(pw + ((wave * 2 + hf) * 64 + lane) * 16) = pb[hf];
     };
 
-    // ---- O^T[dims of this wave][all heads] += V^T . P^T for tile `tp` (P^T
-    // from pbuf[tp & 1]); V^T operands run one 32-dim block ahead.
-    auto pv_phase = [&](int tp) {
-      const DSA_LDS uint8_t *tbp = (const DSA_LDS uint8_t *)kvbuf[tp % kStages];
-      const DSA_LDS uint8_t *pbp = (const DSA_LDS uint8_t *)pbuf[tp & 1];
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        v8bf pbn[NW], av[2];
-#pragma unroll
-        for (int nb = 0; nb < NW; ++nb) pbn[nb] = load_p(pbp, hf, nb);
-        av[0] = load_v(tbp, hf, 0);
-#pragma unroll
-        for (int u = 0; u < MB; ++u) {
-          if (u + 1 < MB) av[(u + 1) & 1] = load_v(tbp, hf, u + 1);
-#pragma unroll
-          for (int nb = 0; nb < NW; ++nb) o[u][nb] = mfma_32x32x16_bf16(av[u & 1], pbn[nb], o[u][nb]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-    };
-
-    // Pipeline: tile t's rows are gathered during step t-1; step t runs QK of
-    // tile t and its softmax, then P.V of tile t-1.
-    // Three tile buffers: t-1 (P.V), t (QK), t+1 (in flight); two P buffers.
+    // Pipeline: tile t's rows are gathered during step t-1; step t runs S^T
+    // of tile t together with P.V of tile t-1, then tile t's softmax.
+    // Three tile buffers: t-1 (P.V), t (S^T), t+1 (in flight); two P buffers.
     // One barrier per step publishes tile t and P(t-1) and frees the buffers
-    // step t+1 overwrites.
+    // step t+1 overwrites.  The first step's P.V multiplies a zero P^T (P
+    // buffer 1, cleared below) with tile 0's rows; the last step's S^T is
+    // discarded -- one code path for every step.
+    {
+      uint8_t *pz = pbuf[1] + tid * (sizeof(pbuf[1]) / T);
+#pragma unroll
+      for (int e = 0; e < (int)(sizeof(pbuf[1]) / T / 16); ++e)
+        reinterpret_cast<v4i *>(pz)[e] = v4i{0, 0, 0, 0};
+    }
     if (ntiles > 0) {
       {
         uint32_t src[kRB];
@@ -393,8 +413,11 @@ void mla_sparse_attn_kernel(AttnArgs p) {
         // memory op of its own is pending inside the loop.
         wait_vmcnt<0>();
         __syncthreads();                  // tile t and P(t-1) visible; buffer (t+1)%3 free
+        const int tp = t > 0 ? t - 1 : 0;
+        const DSA_LDS uint8_t *tbp = (const DSA_LDS uint8_t *)kvbuf[tp % kStages];
+        const DSA_LDS uint8_t *pbp = (const DSA_LDS uint8_t *)pbuf[t > 0 ? (tp & 1) : 1];
+        v16f sc = step_phase(t, tbp, pbp, t + 1 < ntiles);
         if (t < ntiles) {
-          v16f sc = qk_phase(t, t + 1 < ntiles);
           float mt = -INFINITY;
           v8bf pb[2];
           sm_scale(sc, t, 0, 16, mt);
@@ -402,7 +425,6 @@ void mla_sparse_attn_kernel(AttnArgs p) {
           sm_exp(sc, pb, 0, 16);
           sm_store(pb, t);
         }
-        if (t > 0) pv_phase(t - 1);
       }
     }
     // A frame overflow anywhere: redo the token in the frame of its true max.
