@@ -7,26 +7,29 @@
 // at the k-th value toward the lower position (-0.0 == +0.0) and pads with -1
 // when a row has fewer than k causal candidates.
 //
-// One 512-thread workgroup per query row (two fit a CU); the row (n = pos+1 fp32 scores) is
-// read once from HBM in the common case:
+// One 512-thread workgroup per query row (three fit a CU, so one row's select
+// and emission overlap other rows' streaming); the row (n = pos+1 fp32
+// scores) is read once from HBM in the common case:
 //  1. n <= k: every position is selected.
 //  2. Otherwise, a lower bound T_lo on the k-th largest order key comes from
 //     2048 sampled scores (exact select over the sample): the sample rank is
 //     the expected count above the k-th key plus three standard deviations,
 //     so the candidates number about k plus a margin.  For rows that fit the
 //     candidate buffer (n <= kCap) T_lo is the minimum key, i.e. all.
-//  3. One streaming pass (eight 16-byte loads in flight per thread) appends
-//     every (key, position) with key >= T_lo to an LDS candidate buffer: one
-//     prefix scan and one LDS atomic per wave and step; order not kept.
+//  3. One streaming pass (two steps of four 16-byte loads per thread in
+//     flight) writes every (key, position) with key >= T_lo to an LDS
+//     candidate buffer in position order: per step, ballots give each
+//     passing score its rank inside its wave, and one exchange of the wave
+//     totals through LDS gives the rank inside the workgroup.
 //  4. Exact radix select over the candidates gives the k-th key T and the
 //     number of candidates above it.  Because T >= T_lo, every score equal to
 //     T and every score above it is a candidate.
-//  5. Two LDS bitmaps over positions mark "above T" and "equal to T"; popcount
-//     prefix scans over the bitmap words take the lowest-position equal keys
-//     that are needed and emit the selection in ascending position.
-// If the sample was unlucky (fewer than k or more than kCap candidates) or the
-// row is longer than the bitmap, an exact fallback selects with radix passes
-// over the row in global memory and emits it with chunked prefix scans.
+//  5. The candidates are in ascending position, so two prefix scans (ties
+//     seen before each thread's run, then selected before it) emit the
+//     selection in ascending position, taking the lowest-position ties.
+// If the sample was unlucky (fewer than k or more than kCap candidates), an
+// exact fallback selects with radix passes over the row in global memory and
+// emits it with chunked prefix scans.
 #include "common.h"
 #include "launch.h"
 
@@ -35,22 +38,19 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kWavesPerBlock = kThreads / 64;
-constexpr int kCap = 5632;               // candidate buffer entries (key + position); two
+constexpr int kCap = 5632;               // candidate buffer entries (key + position); three
                                          // workgroups' LDS fit one CU
-constexpr int kMaxBitmapN = 131072;      // longest row handled with LDS bitmaps
-constexpr int kBitmapWords = kMaxBitmapN / 32;
 constexpr int kSamples = 2048;           // 64 runs of 32 consecutive scores
 constexpr int kSampleRuns = 64;
+constexpr int kVec = 4;                  // float4 loads per thread and filter step
 
 struct TopkShared {
   uint32_t keys[kCap];
   uint32_t pos[kCap];
-  uint32_t sel[kBitmapWords];
-  uint32_t eq[kBitmapWords];
   uint32_t hist[256];
   uint32_t scan[kWavesPerBlock];
   uint32_t bcast[4];
-  uint32_t count;
+  uint32_t wtot[2][kWavesPerBlock][kVec];  // per step parity: passing scores per wave and slot
 };
 
 // Monotone map fp32 -> uint32 (larger float -> larger key); -0.0 maps like +0.0.
@@ -58,6 +58,12 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
   if (u == 0x80000000u) u = 0u;
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inverse of order_key for keys of finite scores.
+__device__ __forceinline__ float key_to_float(uint32_t key) {
+  const uint32_t u = (key & 0x80000000u) ? (key ^ 0x80000000u) : ~key;
+  return __uint_as_float(u);
 }
 
 __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int lane) {
@@ -242,11 +248,8 @@ void topk_kernel(TopkArgs p) {
     return;
   }
   const float *rowp = p.scores + row * p.ld;
-  if (n > kMaxBitmapN) {
-    select_from_global(rowp, n, k, out, sh);
-    return;
-  }
   const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
   // 2. lower bound on the k-th key from a sample (all keys if the row fits)
   uint32_t t_lo = 0u;
@@ -264,61 +267,97 @@ void topk_kernel(TopkArgs p) {
     uint32_t n_above_s;
     radix_select([&](int64_t i) { return sh.keys[i]; }, kSamples, (uint32_t)j, sh, t_lo, n_above_s);
   }
-  if (tid == 0) sh.count = 0u;
   __syncthreads();
 
-  // 3. candidate filter: one pass over the row; per step each thread loads
-  // 8 float4 (32 scores, 8 contiguous 16 KB blocks across the workgroup).
-  constexpr int kVec = 8;
-  for (int64_t base = 0; base < n; base += (int64_t)kThreads * 4 * kVec) {
-    float4 v[kVec];
+  // 3. candidate filter in position order.  Slot (e, c) of thread tid holds
+  // position base + (e * kThreads + tid) * 4 + c, so position order is slot
+  // e, then wave, then lane, then c: a passing score's rank is the passing
+  // scores of earlier slots e' < e (all waves), of earlier waves in slot e,
+  // of lower lanes in this wave and slot (ballot + mbcnt), and of c' < c.
+  // A score passes when it is >= the sample bound, compared as floats (the
+  // bound is a key of a finite score, so float order and key order agree;
+  // -0 and +0 both compare equal to a zero bound, as their keys do).
+  constexpr int kStep = kThreads * 4 * kVec;
+  const int nn = (int)n;
+  const int n_full = nn / kStep;
+  const float f_lo = t_lo == 0u ? -INFINITY : key_to_float(t_lo);   // key 0: every score passes
+  uint32_t done = 0;   // candidates of the steps before (uniform)
+  auto load_step = [&](int base, float4 (&v)[kVec]) {
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) v[e] = *reinterpret_cast<const float4 *>(rowp + base + (e * kThreads + tid) * 4);
+  };
+  auto filter_step = [&](int base, const float4 (&v)[kVec], bool partial, int par) {
+    uint32_t lane_before[kVec];
 #pragma unroll
     for (int e = 0; e < kVec; ++e) {
-      const int64_t i0 = base + ((int64_t)e * kThreads + tid) * 4;
-      if (i0 + 3 < n) {
-        v[e] = *reinterpret_cast<const float4 *>(rowp + i0);
-      } else {
-        v[e].x = i0 + 0 < n ? rowp[i0 + 0] : 0.f;
-        v[e].y = i0 + 1 < n ? rowp[i0 + 1] : 0.f;
-        v[e].z = i0 + 2 < n ? rowp[i0 + 2] : 0.f;
-        v[e].w = i0 + 3 < n ? rowp[i0 + 3] : 0.f;
-      }
-    }
-    uint32_t pass_bits = 0u;
-#pragma unroll
-    for (int e = 0; e < kVec; ++e) {
-      const int64_t i0 = base + ((int64_t)e * kThreads + tid) * 4;
+      const int i0 = base + (e * kThreads + tid) * 4;
       const float f[4] = {v[e].x, v[e].y, v[e].z, v[e].w};
+      uint32_t tot = 0, below = 0;
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (i0 + c < n && order_key(f[c]) >= t_lo) pass_bits |= 1u << (4 * e + c);
+      for (int c = 0; c < 4; ++c) {
+        const uint64_t m = __ballot((!partial || i0 + c < nn) && f[c] >= f_lo);
+        tot += (uint32_t)__popcll(m);
+        below += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+      }
+      lane_before[e] = below;
+      if (lane == 0) sh.wtot[par][wave][e] = tot;
     }
-    const uint32_t cnt = (uint32_t)__popc(pass_bits);
-    const uint32_t inc = wave_inclusive_scan(cnt, lane);
-    uint32_t wbase = 0;
-    if (lane == 63 && inc > 0) wbase = atomicAdd(&sh.count, inc);
-    wbase = __shfl(wbase, 63, 64);
-    uint32_t at = wbase + inc - cnt;
-    // static loop over the 32 slots (a runtime index into v[] would move it
-    // out of registers)
+    __syncthreads();
+    uint32_t run = done;
 #pragma unroll
     for (int e = 0; e < kVec; ++e) {
+      uint32_t tot = 0, before = 0;
+#pragma unroll
+      for (int w = 0; w < kWavesPerBlock; ++w) {
+        const uint32_t x = sh.wtot[par][w][e];
+        tot += x;
+        before += w < wave ? x : 0u;
+      }
+      uint32_t at = run + before + lane_before[e];
+      run += tot;
+      const int i0 = base + (e * kThreads + tid) * 4;
       const float f[4] = {v[e].x, v[e].y, v[e].z, v[e].w};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        if ((pass_bits >> (4 * e + c)) & 1u) {
+        if ((!partial || i0 + c < nn) && f[c] >= f_lo) {
           if (at < (uint32_t)kCap) {
             sh.keys[at] = order_key(f[c]);
-            sh.pos[at] = (uint32_t)(base + ((int64_t)e * kThreads + tid) * 4 + c);
+            sh.pos[at] = (uint32_t)(i0 + c);
           }
           ++at;
         }
       }
     }
+    done = run;
+  };
+  {
+    float4 va[kVec], vb[kVec];
+    if (n_full > 0) load_step(0, va);
+    for (int st = 0; st < n_full; st += 2) {
+      if (st + 1 < n_full) load_step((st + 1) * kStep, vb);
+      filter_step(st * kStep, va, false, 0);
+      if (st + 1 < n_full) {
+        if (st + 2 < n_full) load_step((st + 2) * kStep, va);
+        filter_step((st + 1) * kStep, vb, false, 1);
+      }
+    }
+    const int tail = n_full * kStep;
+    if (tail < nn) {
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) {
+        const int i0 = tail + (e * kThreads + tid) * 4;
+        float4 x;
+        x.x = i0 + 0 < nn ? rowp[i0 + 0] : 0.f;
+        x.y = i0 + 1 < nn ? rowp[i0 + 1] : 0.f;
+        x.z = i0 + 2 < nn ? rowp[i0 + 2] : 0.f;
+        x.w = i0 + 3 < nn ? rowp[i0 + 3] : 0.f;
+        va[e] = x;
+      }
+      filter_step(tail, va, true, n_full & 1);
+    }
   }
   __syncthreads();
-  const uint32_t cand = sh.count;
-  __syncthreads();
+  const uint32_t cand = done;
   if (cand > (uint32_t)kCap || cand < (uint32_t)k) {
     select_from_global(rowp, n, k, out, sh);
     return;
@@ -329,50 +368,30 @@ void topk_kernel(TopkArgs p) {
   radix_select([&](int64_t i) { return sh.keys[i]; }, cand, (uint32_t)k, sh, thr, n_above);
   const uint32_t need_eq = (uint32_t)k - n_above;
 
-  // 5. bitmaps over positions, then ordered emission
-  const int words = (int)((n + 31) / 32);
-  for (int i = tid; i < words; i += kThreads) {
-    sh.sel[i] = 0u;
-    sh.eq[i] = 0u;
+  // 5. ordered emission: each thread owns a contiguous run of candidates
+  // (ascending positions); ties are taken lowest position first.
+  const uint32_t per = (cand + kThreads - 1) / kThreads;
+  const uint32_t c0 = (uint32_t)tid * per < cand ? (uint32_t)tid * per : cand;
+  const uint32_t c1 = c0 + per < cand ? c0 + per : cand;
+  uint32_t n_sel = 0, n_eq = 0;
+  for (uint32_t i = c0; i < c1; ++i) {
+    const uint32_t key = sh.keys[i];
+    n_sel += key > thr ? 1u : 0u;
+    n_eq += key == thr ? 1u : 0u;
   }
-  __syncthreads();
-  for (uint32_t i = tid; i < cand; i += kThreads) {
-    const uint32_t key = sh.keys[i], ps = sh.pos[i];
-    if (key > thr) atomicOr(&sh.sel[ps >> 5], 1u << (ps & 31));
-    else if (key == thr) atomicOr(&sh.eq[ps >> 5], 1u << (ps & 31));
-  }
-  __syncthreads();
-  // each thread owns a contiguous run of words, so thread order = position order
-  const int wpt = (words + kThreads - 1) / kThreads;
-  const int w0 = tid * wpt, w1 = w0 + wpt < words ? w0 + wpt : words;
-  uint32_t my_eq = 0;
-  for (int w = w0; w < w1; ++w) my_eq += (uint32_t)__popc(sh.eq[w]);
   uint32_t tot;
-  uint32_t eq_before = block_exclusive_scan(my_eq, sh, tot);
-  uint32_t my_sel = 0;
-  for (int w = w0; w < w1; ++w) {
-    uint32_t e = sh.eq[w];
-    const uint32_t pc = (uint32_t)__popc(e);
-    uint32_t take = need_eq > eq_before ? need_eq - eq_before : 0u;
-    if (take > pc) take = pc;
-    uint32_t kept = 0u;
-    for (uint32_t t = 0; t < take; ++t) {
-      kept |= e & (0u - e);   // lowest set bit
-      e &= e - 1u;
+  const uint32_t eq_before = block_exclusive_scan(n_eq, sh, tot);
+  uint32_t take = need_eq > eq_before ? need_eq - eq_before : 0u;
+  if (take > n_eq) take = n_eq;
+  uint32_t at = block_exclusive_scan(n_sel + take, sh, tot);
+  for (uint32_t i = c0; i < c1; ++i) {
+    const uint32_t key = sh.keys[i];
+    bool keep = key > thr;
+    if (key == thr && take > 0u) {
+      keep = true;
+      --take;
     }
-    eq_before += pc;
-    const uint32_t fin = sh.sel[w] | kept;
-    sh.sel[w] = fin;
-    my_sel += (uint32_t)__popc(fin);
-  }
-  uint32_t at = block_exclusive_scan(my_sel, sh, tot);
-  for (int w = w0; w < w1; ++w) {
-    uint32_t f = sh.sel[w];
-    while (f) {
-      const int bit = __builtin_ctz(f);
-      f &= f - 1u;
-      out[at++] = w * 32 + bit;
-    }
+    if (keep) out[at++] = (int32_t)sh.pos[i];
   }
 }
 

@@ -111,7 +111,7 @@ def test_topk_ties_signed_zeros_and_fallbacks():
         rng.integers(-3, 4, 20000).astype(np.float32),                      # heavy duplicates
         np.full(40000, -1.0, np.float32),                                   # long all-equal
         np.concatenate([np.zeros(30000, np.float32), np.ones(100, np.float32)]),
-        rng.standard_normal(140000).astype(np.float32),                     # longer than bitmap
+        rng.standard_normal(140000).astype(np.float32),                     # longer than 2^17
         np.arange(20000, dtype=np.float32)[::-1].copy(),                    # sorted descending
         np.arange(20000, dtype=np.float32),                                 # sorted ascending
     ]
