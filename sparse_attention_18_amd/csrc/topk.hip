@@ -12,7 +12,8 @@
 // scores) is read once from HBM in the common case:
 //  1. n <= k: every position is selected.
 //  2. Otherwise, a lower bound T_lo on the k-th largest order key comes from
-//     2048 sampled scores (exact select over the sample): the sample rank is
+//     2048 sampled scores (a 16-bit radix select over the sample; the lower
+//     edge of the bin holding the sample's rank-j key): the sample rank is
 //     the expected count above the k-th key plus three standard deviations,
 //     so the candidates number about k plus a margin.  For rows that fit the
 //     candidate buffer (n <= kCap) T_lo is the minimum key, i.e. all.
@@ -112,9 +113,12 @@ __device__ __forceinline__ uint32_t block_or(uint32_t v, TopkShared &sh, bool is
 // Exact select: the kth-largest (1-based) key among `count` keys read through
 // `get(i)`, and how many keys are strictly larger.  Radix passes of up to 8
 // bits, most significant first, after skipping the bits every key shares.
+// With max_passes < 4 it stops early and returns the lower edge of the radix
+// bin that holds the kth-largest key: a lower bound on that key (n_above is
+// then the count above the bin).
 template <typename Get>
 __device__ void radix_select(Get get, int64_t count, uint32_t kth, TopkShared &sh, uint32_t &thr,
-                             uint32_t &n_above) {
+                             uint32_t &n_above, int max_passes = 4) {
   const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63;
   uint32_t vor = 0u, vand = 0xFFFFFFFFu;
   for (int64_t i = tid; i < count; i += kThreads) {
@@ -134,7 +138,7 @@ __device__ void radix_select(Get get, int64_t count, uint32_t kth, TopkShared &s
   uint32_t prefix = shift == 32 ? 0u : (vor >> shift) << shift;
   uint32_t mask = shift == 32 ? 0u : ~((1u << shift) - 1u);
   uint32_t kk = kth;
-  while (shift > 0) {
+  for (int pass = 0; shift > 0 && pass < max_passes; ++pass) {
     const int nb = shift < 8 ? shift : 8;
     shift -= nb;
     const uint32_t dmask = (1u << nb) - 1u;
@@ -251,6 +255,19 @@ void topk_kernel(TopkArgs p) {
   const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
+  // The first two filter steps do not depend on the sample bound: their loads
+  // go out first, so that their latency overlaps the sample phase.
+  constexpr int kStep = kThreads * 4 * kVec;
+  const int nn = (int)n;
+  const int n_full = nn / kStep;
+  auto load_step = [&](int base, float4 (&v)[kVec]) {
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) v[e] = *reinterpret_cast<const float4 *>(rowp + base + (e * kThreads + tid) * 4);
+  };
+  float4 va[kVec], vb[kVec];
+  if (n_full > 0) load_step(0, va);
+  if (n_full > 1) load_step(kStep, vb);
+
   // 2. lower bound on the k-th key from a sample (all keys if the row fits)
   uint32_t t_lo = 0u;
   if (n > kCap) {
@@ -265,7 +282,10 @@ void topk_kernel(TopkArgs p) {
     int64_t j = (int64_t)(expect + 3.0 * sqrt(expect) + 4.0);
     if (j > kSamples) j = kSamples;
     uint32_t n_above_s;
-    radix_select([&](int64_t i) { return sh.keys[i]; }, kSamples, (uint32_t)j, sh, t_lo, n_above_s);
+    // two radix passes (16 bits below the shared prefix) are enough: the
+    // bin's lower edge is a valid lower bound, and a bin that narrow adds
+    // few scores
+    radix_select([&](int64_t i) { return sh.keys[i]; }, kSamples, (uint32_t)j, sh, t_lo, n_above_s, 2);
   }
   __syncthreads();
 
@@ -277,15 +297,8 @@ void topk_kernel(TopkArgs p) {
   // A score passes when it is >= the sample bound, compared as floats (the
   // bound is a key of a finite score, so float order and key order agree;
   // -0 and +0 both compare equal to a zero bound, as their keys do).
-  constexpr int kStep = kThreads * 4 * kVec;
-  const int nn = (int)n;
-  const int n_full = nn / kStep;
   const float f_lo = t_lo == 0u ? -INFINITY : key_to_float(t_lo);   // key 0: every score passes
   uint32_t done = 0;   // candidates of the steps before (uniform)
-  auto load_step = [&](int base, float4 (&v)[kVec]) {
-#pragma unroll
-    for (int e = 0; e < kVec; ++e) v[e] = *reinterpret_cast<const float4 *>(rowp + base + (e * kThreads + tid) * 4);
-  };
   auto filter_step = [&](int base, const float4 (&v)[kVec], bool partial, int par) {
     uint32_t lane_before[kVec];
 #pragma unroll
@@ -331,14 +344,13 @@ void topk_kernel(TopkArgs p) {
     done = run;
   };
   {
-    float4 va[kVec], vb[kVec];
-    if (n_full > 0) load_step(0, va);
+    // steps st and st+1 are in flight when step st is filtered
     for (int st = 0; st < n_full; st += 2) {
-      if (st + 1 < n_full) load_step((st + 1) * kStep, vb);
       filter_step(st * kStep, va, false, 0);
+      if (st + 2 < n_full) load_step((st + 2) * kStep, va);
       if (st + 1 < n_full) {
-        if (st + 2 < n_full) load_step((st + 2) * kStep, va);
         filter_step((st + 1) * kStep, vb, false, 1);
+        if (st + 3 < n_full) load_step((st + 3) * kStep, vb);
       }
     }
     const int tail = n_full * kStep;
