@@ -107,7 +107,12 @@ dsa_status dsa_indexer_scores(const dsa_problem *p, const uint8_t *q_fp8, const 
  *   scores [total_q, ld_scores] float (read on 0..pos(r) only)
  *   topk_idx [total_q, k] int32
  * workspace / workspace_bytes: at least dsa_workspace_bytes(p, DSA_WS_TOPK)
- * bytes of device memory (may be NULL when that is 0).
+ * bytes of 16-byte aligned device memory (may be NULL when that is 0).  It is
+ * zero for batches of more than 512 rows or contexts under 32768; smaller
+ * batches of long rows cut each row into segments (at most 32, and few
+ * enough that all of them run at once), one workgroup each, whose candidate
+ * lists (5632 slots of 8 bytes per segment) live there.
+ * Contents need no initialisation and are not preserved.
  */
 dsa_status dsa_topk(const dsa_problem *p, const float *scores, int64_t ld_scores,
                     int32_t *topk_idx, void *workspace, size_t workspace_bytes, void *stream);

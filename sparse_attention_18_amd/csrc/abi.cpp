@@ -155,13 +155,18 @@ dsa::AttnArgs attn_args(const dsa_problem *p, const uint16_t *q, const uint16_t 
   return a;
 }
 
-dsa::TopkArgs topk_args(const dsa_problem *p, const float *scores, int64_t ld, int32_t *idx) {
+dsa::TopkArgs topk_args(const dsa_problem *p, const float *scores, int64_t ld, int32_t *idx,
+                        void *ws = nullptr, size_t wsb = 0) {
   dsa::TopkArgs a;
   a.seq = layout_of(p);
   a.scores = scores;
   a.ld = ld;
   a.idx = idx;
   a.k = p->topk;
+  a.workspace = ws;
+  a.workspace_bytes = wsb;
+  a.seg_len = 0;
+  a.nseg = 0;
   return a;
 }
 
@@ -267,7 +272,10 @@ dsa_status dsa_topk(const dsa_problem *p, const float *scores, int64_t ld_scores
   const size_t need = ws_topk(p, ld_scores);
   DSA_CHECK(workspace_bytes >= need && (need == 0 || workspace != nullptr), DSA_ERR_WORKSPACE,
             "top-k workspace needs %zu bytes (got %zu)", need, workspace_bytes);
-  return hip_status(dsa::launch_topk(topk_args(p, scores, ld_scores, topk_idx),
+  DSA_CHECK(need == 0 || aligned16(workspace), DSA_ERR_INVALID_ARGUMENT,
+            "workspace must be 16-byte aligned");
+  return hip_status(dsa::launch_topk(topk_args(p, scores, ld_scores, topk_idx, workspace,
+                                               workspace_bytes),
                                      static_cast<hipStream_t>(stream)),
                     "top-k launch");
 }
@@ -314,8 +322,8 @@ dsa_status dsa_forward(const dsa_problem *p, const uint8_t *q_fp8, const float *
   DSA_TRY(hip_status(dsa::launch_indexer(indexer_args(p, q_fp8, q_scale, w, k_fp8, k_scale,
                                                       scores, ld), st),
                      "indexer launch"));
-  DSA_TRY(hip_status(dsa::launch_topk(topk_args(p, scores, ld, idx), st), "top-k launch"));
-  (void)topk_ws;
+  DSA_TRY(hip_status(dsa::launch_topk(topk_args(p, scores, ld, idx, topk_ws, ws.topk), st),
+                     "top-k launch"));
   return hip_status(dsa::launch_sparse_attn(attn_args(p, q, kv, idx, out, lse, attn_ws, ws.attn),
                                             st),
                     "attention launch");

@@ -84,6 +84,30 @@ __device__ __forceinline__ float sum_across_halves(float a) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Inclusive scan over the 64 lanes of a wave with DPP moves (no LDS round
+// trip): Hillis-Steele steps 1, 2, 4, 8 inside each 16-lane row (row_shr;
+// lanes whose source falls outside the row read the identity), then lane 15
+// of rows 0 and 2 is added into rows 1 and 3 (row_bcast:15) and lane 31 into
+// rows 2 and 3 (row_bcast:31).  Op: 0 sum, 1 bitwise or, 2 bitwise and.
+template <int Op>
+__device__ __forceinline__ uint32_t wave_scan(uint32_t v) {
+  constexpr int id = Op == 2 ? -1 : 0;
+  auto f = [](uint32_t a, uint32_t b) { return Op == 0 ? a + b : (Op == 1 ? (a | b) : (a & b)); };
+  v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x111, 0xf, 0xf, false));  // row_shr:1
+  v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x112, 0xf, 0xf, false));  // row_shr:2
+  v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x114, 0xf, 0xf, false));  // row_shr:4
+  v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x118, 0xf, 0xf, false));  // row_shr:8
+  v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = f(v, (uint32_t)__builtin_amdgcn_update_dpp(id, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return v;
+}
+
+// The scan's value in lane 63: the whole wave's sum / or / and (uniform).
+template <int Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_scan<Op>(v), 63);
+}
+
 // fp32 -> bf16 bits, round to nearest even (inputs are finite here).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   uint32_t u = __float_as_uint(f);

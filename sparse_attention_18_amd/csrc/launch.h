@@ -35,6 +35,9 @@ struct TopkArgs {
   int64_t ld;
   int32_t *idx;
   int32_t k;
+  void *workspace;
+  size_t workspace_bytes;
+  int32_t seg_len, nseg;   // few-rows path: scores per segment, segments per row (set by the launcher)
 };
 
 struct AttnArgs {

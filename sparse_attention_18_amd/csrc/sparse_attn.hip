@@ -202,12 +202,7 @@ void mla_sparse_attn_kernel(AttnArgs p) {
       vals[e] = (v >= 0 && v < s.kvlen) ? v : -1;
       cnt += vals[e] >= 0;
     }
-    int inc = cnt;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int y = __shfl_up(inc, d, 64);
-      if (lane >= d) inc += y;
-    }
+    const int inc = (int)wave_scan<0>((uint32_t)cnt);
     if (lane == 63) s_scan[wave] = inc;
     if (tid == 0) s_flag = 0;
     __syncthreads();

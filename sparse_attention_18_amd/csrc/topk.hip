@@ -31,6 +31,8 @@
 // If the sample was unlucky (fewer than k or more than kCap candidates), an
 // exact fallback selects with radix passes over the row in global memory and
 // emits it with chunked prefix scans.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -44,12 +46,15 @@ constexpr int kCap = 5632;               // candidate buffer entries (key + posi
 constexpr int kSamples = 2048;           // 64 runs of 32 consecutive scores
 constexpr int kSampleRuns = 64;
 constexpr int kVec = 4;                  // float4 loads per thread and filter step
+constexpr int kMaxSegs = 32;             // segments per row in the few-rows path
+constexpr int kSplitRows = 512;          // batches up to this many rows use that path
 
 struct TopkShared {
   uint32_t keys[kCap];
   uint32_t pos[kCap];
   uint32_t hist[256];
   uint32_t scan[kWavesPerBlock];
+  uint32_t scan2[kWavesPerBlock];
   uint32_t bcast[4];
   uint32_t wtot[2][kWavesPerBlock][kVec];  // per step parity: passing scores per wave and slot
 };
@@ -67,24 +72,15 @@ __device__ __forceinline__ float key_to_float(uint32_t key) {
   return __uint_as_float(u);
 }
 
-__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v, int lane) {
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t t = __shfl_up(v, d, 64);
-    if (lane >= d) v += t;
-  }
-  return v;
-}
-
 // Exclusive scan over the workgroup in thread order; also returns the total.
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, TopkShared &sh, uint32_t &total) {
   const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63, wave = tid >> 6;
-  const uint32_t inc = wave_inclusive_scan(v, lane);
+  const uint32_t inc = wave_scan<0>(v);
   if (lane == 63) sh.scan[wave] = inc;
   __syncthreads();
   if (wave == 0) {
     uint32_t x = lane < kWavesPerBlock ? sh.scan[lane] : 0u;
-    const uint32_t xi = wave_inclusive_scan(x, lane);
+    const uint32_t xi = wave_scan<0>(x);
     if (lane < kWavesPerBlock) sh.scan[lane] = xi - x;
     if (lane == kWavesPerBlock - 1) sh.bcast[3] = xi;
   }
@@ -95,19 +91,23 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, TopkShared 
   return r;
 }
 
-__device__ __forceinline__ uint32_t block_or(uint32_t v, TopkShared &sh, bool is_and) {
+// Bitwise or and and of every thread's key over the workgroup.
+__device__ __forceinline__ void block_or_and(uint32_t &vor, uint32_t &vand, TopkShared &sh) {
   const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63, wave = tid >> 6;
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    const uint32_t t = __shfl_xor(v, d, 64);
-    v = is_and ? (v & t) : (v | t);
+  const uint32_t o = wave_reduce<1>(vor), a = wave_reduce<2>(vand);
+  if (lane == 0) {
+    sh.scan[wave] = o;
+    sh.scan2[wave] = a;
   }
-  if (lane == 0) sh.scan[wave] = v;
   __syncthreads();
-  uint32_t r = sh.scan[0];
-  for (int i = 1; i < kWavesPerBlock; ++i) r = is_and ? (r & sh.scan[i]) : (r | sh.scan[i]);
+  vor = sh.scan[0];
+  vand = sh.scan2[0];
+#pragma unroll
+  for (int i = 1; i < kWavesPerBlock; ++i) {
+    vor |= sh.scan[i];
+    vand &= sh.scan2[i];
+  }
   __syncthreads();
-  return r;
 }
 
 // Exact select: the kth-largest (1-based) key among `count` keys read through
@@ -126,8 +126,7 @@ __device__ void radix_select(Get get, int64_t count, uint32_t kth, TopkShared &s
     vor |= k;
     vand &= k;
   }
-  vor = block_or(vor, sh, false);
-  vand = block_or(vand, sh, true);
+  block_or_and(vor, vand, sh);
   const uint32_t diff = vor ^ vand;
   n_above = 0;
   if (diff == 0u) {            // all keys equal
@@ -157,7 +156,7 @@ __device__ void radix_select(Get get, int64_t count, uint32_t kth, TopkShared &s
         c[i] = sh.hist[255 - 4 * lane - i];
         s += c[i];
       }
-      const uint32_t inc = wave_inclusive_scan(s, lane);
+      const uint32_t inc = wave_scan<0>(s);
       const uint32_t exc = inc - s;
       const bool hit = exc < kk && inc >= kk;
       if (hit) {
@@ -234,49 +233,22 @@ __device__ void select_from_global(const float *row, int64_t n, int k, int32_t *
   }
 }
 
-__global__ __launch_bounds__(kThreads)
-void topk_kernel(TopkArgs p) {
-  __shared__ TopkShared sh;
-  const int64_t row = __builtin_amdgcn_workgroup_id_x();
-  const int b = find_seq(p.seq, row);
-  const SeqInfo s = load_seq(p.seq, b);
-  int32_t *out = p.idx + row * p.k;
-  if (row < s.q0 || row >= s.q1 || s.kvlen <= 0) {
-    emit_all(out, 0, p.k);
-    return;
-  }
-  const int64_t n = row_pos(s, row) + 1;
-  const int k = p.k;
-  if (n <= k) {
-    emit_all(out, n, k);
-    return;
-  }
-  const float *rowp = p.scores + row * p.ld;
-  const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-  // The first two filter steps do not depend on the sample bound: their loads
-  // go out first, so that their latency overlaps the sample phase.
-  constexpr int kStep = kThreads * 4 * kVec;
-  const int nn = (int)n;
-  const int n_full = nn / kStep;
-  auto load_step = [&](int base, float4 (&v)[kVec]) {
-#pragma unroll
-    for (int e = 0; e < kVec; ++e) v[e] = *reinterpret_cast<const float4 *>(rowp + base + (e * kThreads + tid) * 4);
-  };
-  float4 va[kVec], vb[kVec];
-  if (n_full > 0) load_step(0, va);
-  if (n_full > 1) load_step(kStep, vb);
-
-  // 2. lower bound on the k-th key from a sample (all keys if the row fits)
+// Lower bound on the k-th largest key of a row with n > kCap scores, from
+// 2048 sampled scores (uniform over the workgroup; 0 when every score passes).
+__device__ uint32_t sample_bound(const float *rowp, int64_t n, int k, TopkShared &sh) {
   uint32_t t_lo = 0u;
   if (n > kCap) {
+    const int tid = (int)__builtin_amdgcn_workitem_id_x();
     const int64_t span = n - 32;
-    for (int i = tid; i < kSamples; i += kThreads) {
-      const int run = i >> 5, off = i & 31;
-      const int64_t start = span * run / (kSampleRuns - 1);
-      sh.keys[i] = order_key(rowp[start + off]);
+    constexpr int kPer = kSamples / kThreads;
+    float v[kPer];   // all loads in flight before the first LDS store
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+      const int i = tid + u * kThreads, run = i >> 5, off = i & 31;
+      v[u] = rowp[span * run / (kSampleRuns - 1) + off];
     }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) sh.keys[tid + u * kThreads] = order_key(v[u]);
     __syncthreads();
     const double expect = (double)kSamples * (double)k / (double)n;
     int64_t j = (int64_t)(expect + 3.0 * sqrt(expect) + 4.0);
@@ -288,16 +260,49 @@ void topk_kernel(TopkArgs p) {
     radix_select([&](int64_t i) { return sh.keys[i]; }, kSamples, (uint32_t)j, sh, t_lo, n_above_s, 2);
   }
   __syncthreads();
+  return t_lo;
+}
 
-  // 3. candidate filter in position order.  Slot (e, c) of thread tid holds
-  // position base + (e * kThreads + tid) * 4 + c, so position order is slot
-  // e, then wave, then lane, then c: a passing score's rank is the passing
-  // scores of earlier slots e' < e (all waves), of earlier waves in slot e,
-  // of lower lanes in this wave and slot (ballot + mbcnt), and of c' < c.
-  // A score passes when it is >= the sample bound, compared as floats (the
-  // bound is a key of a finite score, so float order and key order agree;
-  // -0 and +0 both compare equal to a zero bound, as their keys do).
-  const float f_lo = t_lo == 0u ? -INFINITY : key_to_float(t_lo);   // key 0: every score passes
+constexpr int kStep = kThreads * 4 * kVec;   // scores per filter step
+
+__device__ __forceinline__ void load_step(const float *rowp, int base, float4 (&v)[kVec]) {
+  const int tid = (int)__builtin_amdgcn_workitem_id_x();
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) v[e] = *reinterpret_cast<const float4 *>(rowp + base + (e * kThreads + tid) * 4);
+}
+
+// Candidate sinks: entry `at` of the position-ordered candidate list.
+struct LdsSink {
+  TopkShared *sh;
+  __device__ void put(uint32_t at, uint32_t key, uint32_t pos) const {
+    if (at < (uint32_t)kCap) {
+      sh->keys[at] = key;
+      sh->pos[at] = pos;
+    }
+  }
+};
+struct GlobalSink {
+  uint2 *c;
+  __device__ void put(uint32_t at, uint32_t key, uint32_t pos) const {
+    if (at < (uint32_t)kCap) c[at] = make_uint2(key, pos);
+  }
+};
+
+// Candidate filter over scores [lo, hi) of a row (lo a multiple of 4 floats
+// from a 16-byte aligned row), in position order.  va / vb must already hold
+// steps 0 and 1 of the range where those are full steps.  Slot (e, c) of
+// thread tid holds position base + (e * kThreads + tid) * 4 + c, so position
+// order is slot e, then wave, then lane, then c: a passing score's rank is
+// the passing scores of earlier slots e' < e (all waves), of earlier waves in
+// slot e, of lower lanes in this wave and slot (ballot + mbcnt), and of
+// c' < c.  A score passes when it is >= f_lo.  Returns the number of passing
+// scores (uniform; entries at or past kCap are counted but not stored).
+template <class Sink>
+__device__ uint32_t filter_range(const float *rowp, int lo, int hi, float f_lo, const Sink &sink,
+                                 TopkShared &sh, float4 (&va)[kVec], float4 (&vb)[kVec]) {
+  const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n_full = (hi - lo) / kStep;
   uint32_t done = 0;   // candidates of the steps before (uniform)
   auto filter_step = [&](int base, const float4 (&v)[kVec], bool partial, int par) {
     uint32_t lane_before[kVec];
@@ -308,7 +313,7 @@ void topk_kernel(TopkArgs p) {
       uint32_t tot = 0, below = 0;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint64_t m = __ballot((!partial || i0 + c < nn) && f[c] >= f_lo);
+        const uint64_t m = __ballot((!partial || i0 + c < hi) && f[c] >= f_lo);
         tot += (uint32_t)__popcll(m);
         below += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
       }
@@ -332,49 +337,44 @@ void topk_kernel(TopkArgs p) {
       const float f[4] = {v[e].x, v[e].y, v[e].z, v[e].w};
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        if ((!partial || i0 + c < nn) && f[c] >= f_lo) {
-          if (at < (uint32_t)kCap) {
-            sh.keys[at] = order_key(f[c]);
-            sh.pos[at] = (uint32_t)(i0 + c);
-          }
+        if ((!partial || i0 + c < hi) && f[c] >= f_lo) {
+          sink.put(at, order_key(f[c]), (uint32_t)(i0 + c));
           ++at;
         }
       }
     }
     done = run;
   };
-  {
-    // steps st and st+1 are in flight when step st is filtered
-    for (int st = 0; st < n_full; st += 2) {
-      filter_step(st * kStep, va, false, 0);
-      if (st + 2 < n_full) load_step((st + 2) * kStep, va);
-      if (st + 1 < n_full) {
-        filter_step((st + 1) * kStep, vb, false, 1);
-        if (st + 3 < n_full) load_step((st + 3) * kStep, vb);
-      }
+  // steps st and st+1 are in flight when step st is filtered
+  for (int st = 0; st < n_full; st += 2) {
+    filter_step(lo + st * kStep, va, false, 0);
+    if (st + 2 < n_full) load_step(rowp, lo + (st + 2) * kStep, va);
+    if (st + 1 < n_full) {
+      filter_step(lo + (st + 1) * kStep, vb, false, 1);
+      if (st + 3 < n_full) load_step(rowp, lo + (st + 3) * kStep, vb);
     }
-    const int tail = n_full * kStep;
-    if (tail < nn) {
+  }
+  const int tail = lo + n_full * kStep;
+  if (tail < hi) {
 #pragma unroll
-      for (int e = 0; e < kVec; ++e) {
-        const int i0 = tail + (e * kThreads + tid) * 4;
-        float4 x;
-        x.x = i0 + 0 < nn ? rowp[i0 + 0] : 0.f;
-        x.y = i0 + 1 < nn ? rowp[i0 + 1] : 0.f;
-        x.z = i0 + 2 < nn ? rowp[i0 + 2] : 0.f;
-        x.w = i0 + 3 < nn ? rowp[i0 + 3] : 0.f;
-        va[e] = x;
-      }
-      filter_step(tail, va, true, n_full & 1);
+    for (int e = 0; e < kVec; ++e) {
+      const int i0 = tail + (e * kThreads + tid) * 4;
+      float4 x;
+      x.x = i0 + 0 < hi ? rowp[i0 + 0] : 0.f;
+      x.y = i0 + 1 < hi ? rowp[i0 + 1] : 0.f;
+      x.z = i0 + 2 < hi ? rowp[i0 + 2] : 0.f;
+      x.w = i0 + 3 < hi ? rowp[i0 + 3] : 0.f;
+      va[e] = x;
     }
+    filter_step(tail, va, true, n_full & 1);
   }
   __syncthreads();
-  const uint32_t cand = done;
-  if (cand > (uint32_t)kCap || cand < (uint32_t)k) {
-    select_from_global(rowp, n, k, out, sh);
-    return;
-  }
+  return done;
+}
 
+// Steps 4 and 5 over a position-ordered candidate list in LDS (k <= cand <= kCap).
+__device__ void select_and_emit(uint32_t cand, int k, int32_t *out, TopkShared &sh) {
+  const int tid = (int)__builtin_amdgcn_workitem_id_x();
   // 4. exact k-th key among the candidates
   uint32_t thr, n_above;
   radix_select([&](int64_t i) { return sh.keys[i]; }, cand, (uint32_t)k, sh, thr, n_above);
@@ -407,13 +407,181 @@ void topk_kernel(TopkArgs p) {
   }
 }
 
+// One workgroup per row (batches with enough rows to fill the chip).
+__global__ __launch_bounds__(kThreads)
+void topk_kernel(TopkArgs p) {
+  __shared__ TopkShared sh;
+  const int64_t row = __builtin_amdgcn_workgroup_id_x();
+  const int b = find_seq(p.seq, row);
+  const SeqInfo s = load_seq(p.seq, b);
+  int32_t *out = p.idx + row * p.k;
+  if (row < s.q0 || row >= s.q1 || s.kvlen <= 0) {
+    emit_all(out, 0, p.k);
+    return;
+  }
+  const int64_t n = row_pos(s, row) + 1;
+  const int k = p.k;
+  if (n <= k) {
+    emit_all(out, n, k);
+    return;
+  }
+  const float *rowp = p.scores + row * p.ld;
+  const int nn = (int)n;
+
+  // The first two filter steps do not depend on the sample bound: their loads
+  // go out first, so that their latency overlaps the sample phase.
+  float4 va[kVec], vb[kVec];
+  if (nn / kStep > 0) load_step(rowp, 0, va);
+  if (nn / kStep > 1) load_step(rowp, kStep, vb);
+  const uint32_t t_lo = sample_bound(rowp, n, k, sh);
+  // the bound is a key of a finite score, so float order and key order agree
+  // (-0 and +0 both compare equal to a zero bound, as their keys do); key 0
+  // lets every score pass
+  const float f_lo = t_lo == 0u ? -INFINITY : key_to_float(t_lo);
+  const uint32_t cand = filter_range(rowp, 0, nn, f_lo, LdsSink{&sh}, sh, va, vb);
+  if (cand > (uint32_t)kCap || cand < (uint32_t)k) {
+    select_from_global(rowp, n, k, out, sh);
+    return;
+  }
+  select_and_emit(cand, k, out, sh);
+}
+
+// Few rows (decode): each row is cut into segments of seg_len scores, one
+// workgroup each.  Every segment's workgroup derives the same sample bound
+// from the whole row, filters its own segment and writes its candidates, in
+// position order, to a fixed slot of the workspace together with their
+// count; the segments' lists concatenated are exactly the list the
+// one-workgroup filter builds.
+__global__ __launch_bounds__(kThreads)
+void topk_segment_kernel(TopkArgs p, uint32_t *counts, uint2 *cands) {
+  __shared__ TopkShared sh;
+  const int64_t row = __builtin_amdgcn_workgroup_id_y();
+  const int seg = __builtin_amdgcn_workgroup_id_x();
+  const int b = find_seq(p.seq, row);
+  const SeqInfo s = load_seq(p.seq, b);
+  if (row < s.q0 || row >= s.q1 || s.kvlen <= 0) return;
+  const int64_t n = row_pos(s, row) + 1;
+  const int k = p.k;
+  const int lo = seg * p.seg_len;
+  if (n <= k || lo >= n) return;
+  const int hi = n - lo > p.seg_len ? lo + p.seg_len : (int)n;
+  const float *rowp = p.scores + row * p.ld;
+  float4 va[kVec], vb[kVec];
+  if ((hi - lo) / kStep > 0) load_step(rowp, lo, va);
+  if ((hi - lo) / kStep > 1) load_step(rowp, lo + kStep, vb);
+  const uint32_t t_lo = sample_bound(rowp, n, k, sh);
+  const float f_lo = t_lo == 0u ? -INFINITY : key_to_float(t_lo);
+  const size_t slot = (size_t)row * p.nseg + seg;
+  const uint32_t cand = filter_range(rowp, lo, hi, f_lo, GlobalSink{cands + slot * kCap}, sh, va, vb);
+  if (__builtin_amdgcn_workitem_id_x() == 0) counts[slot] = cand;
+}
+
+// Merge of a row's segment lists: one workgroup per row.
+__global__ __launch_bounds__(kThreads)
+void topk_merge_kernel(TopkArgs p, const uint32_t *counts, const uint2 *cands) {
+  __shared__ TopkShared sh;
+  const int64_t row = __builtin_amdgcn_workgroup_id_x();
+  const int b = find_seq(p.seq, row);
+  const SeqInfo s = load_seq(p.seq, b);
+  int32_t *out = p.idx + row * p.k;
+  if (row < s.q0 || row >= s.q1 || s.kvlen <= 0) {
+    emit_all(out, 0, p.k);
+    return;
+  }
+  const int64_t n = row_pos(s, row) + 1;
+  const int k = p.k;
+  if (n <= k) {
+    emit_all(out, n, k);
+    return;
+  }
+  const int tid = (int)__builtin_amdgcn_workitem_id_x();
+  const int nseg = (int)((n + p.seg_len - 1) / p.seg_len);
+  const uint32_t *cnt = counts + (size_t)row * p.nseg;
+  // segment offsets by an exclusive scan over the (at most kThreads) counts
+  const uint32_t c = tid < nseg ? cnt[tid] : 0u;
+  uint32_t total;
+  const uint32_t off = block_exclusive_scan(c > (uint32_t)kCap ? (uint32_t)kCap + 1u : c, sh, total);
+  if (total > (uint32_t)kCap || total < (uint32_t)k) {
+    select_from_global(p.scores + row * p.ld, n, k, out, sh);
+    return;
+  }
+  // copy the segment lists into LDS at their offsets: wave w copies
+  // segments w, w + 8, ...  (nseg <= kMaxSegs, so hist holds both arrays)
+  if (tid < nseg) {
+    sh.hist[tid] = off;
+    sh.hist[kMaxSegs + tid] = c;
+  }
+  __syncthreads();
+  const int lane = tid & 63, wave = tid >> 6;
+  const uint2 *src = cands + (size_t)row * p.nseg * kCap;
+  for (int sgi = wave; sgi < nseg; sgi += kWavesPerBlock) {
+    const uint32_t o = sh.hist[sgi], cs = sh.hist[kMaxSegs + sgi];
+    for (uint32_t i0 = lane; i0 < cs; i0 += 64 * 8) {
+      uint2 v[8];   // eight loads in flight before the LDS stores
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t i = i0 + 64 * u;
+        if (i < cs) v[u] = src[(size_t)sgi * kCap + i];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t i = i0 + 64 * u;
+        if (i < cs) {
+          sh.keys[o + i] = v[u].x;
+          sh.pos[o + i] = v[u].y;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  select_and_emit(total, k, out, sh);
+}
 }  // namespace
 
-size_t topk_workspace_bytes(const TopkArgs &) { return 0; }
+namespace {
+
+// Segment geometry of the few-rows path; false when the one-workgroup-per-row
+// kernel serves the batch.
+bool split_geometry(const TopkArgs &a, int32_t &seg_len, int32_t &nseg) {
+  if (a.seq.total_q > kSplitRows || a.seq.max_kv_len < 4 * (int64_t)kStep) return false;
+  // as many segments as fit one round of workgroups (three per CU on 256
+  // CUs), at most kMaxSegs per row
+  const int64_t steps = (a.seq.max_kv_len + kStep - 1) / kStep;
+  const int64_t per_row = std::max<int64_t>(1, std::min<int64_t>(kMaxSegs, 768 / a.seq.total_q));
+  const int64_t seg_steps = (steps + per_row - 1) / per_row;
+  seg_len = (int32_t)(seg_steps * kStep);
+  nseg = (int32_t)((a.seq.max_kv_len + seg_len - 1) / seg_len);
+  return true;
+}
+
+size_t split_bytes(const TopkArgs &a, int32_t nseg) {
+  const size_t slots = (size_t)a.seq.total_q * (size_t)nseg;
+  return ((slots * sizeof(uint32_t) + 255) / 256) * 256 + slots * kCap * sizeof(uint2);
+}
+
+}  // namespace
+
+size_t topk_workspace_bytes(const TopkArgs &a) {
+  int32_t seg_len, nseg;
+  return split_geometry(a, seg_len, nseg) ? split_bytes(a, nseg) : 0;
+}
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t stream) {
   if (a.seq.total_q == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)a.seq.total_q), dim3(kThreads), 0, stream, a);
+  TopkArgs s = a;
+  if (split_geometry(a, s.seg_len, s.nseg) && a.workspace != nullptr &&
+      a.workspace_bytes >= split_bytes(a, s.nseg)) {
+    const size_t slots = (size_t)a.seq.total_q * (size_t)s.nseg;
+    uint32_t *counts = static_cast<uint32_t *>(a.workspace);
+    uint2 *cands = reinterpret_cast<uint2 *>(static_cast<uint8_t *>(a.workspace) +
+                                             ((slots * sizeof(uint32_t) + 255) / 256) * 256);
+    hipLaunchKernelGGL(topk_segment_kernel, dim3((unsigned)s.nseg, (unsigned)a.seq.total_q),
+                       dim3(kThreads), 0, stream, s, counts, cands);
+    hipLaunchKernelGGL(topk_merge_kernel, dim3((unsigned)a.seq.total_q), dim3(kThreads), 0, stream,
+                       s, counts, cands);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(topk_kernel, dim3((unsigned)a.seq.total_q), dim3(kThreads), 0, stream, s);
   return hipGetLastError();
 }
 

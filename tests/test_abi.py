@@ -118,6 +118,27 @@ def test_topk_rejects_bad_ld_and_index_pointer():
     assert "topk_idx" in _msg()
 
 
+def test_topk_workspace_for_few_long_rows():
+    """Few rows with long contexts split every row over several workgroups and
+    need room for the segments' candidate lists; large batches need none."""
+    lib = binding.load_library()
+    big = _problem()
+    assert lib.dsa_workspace_bytes(ctypes.byref(big), binding.WS_TOPK) == 0
+    dec = _problem(batch=64, total_q=64, max_q_len=1, total_kv=64 * 131072, max_kv_len=131072)
+    need = lib.dsa_workspace_bytes(ctypes.byref(dec), binding.WS_TOPK)
+    # 8 segments of 16384 scores per row (8 x 64 workgroups fit one round on
+    # the chip), 5632 (key, position) slots each
+    assert need >= 64 * 8 * 5632 * 8
+    assert lib.dsa_topk(ctypes.byref(dec), FAKE, 131072, FAKE, None, 0, None) == \
+        binding.DSA_ERR_WORKSPACE
+    assert "top-k workspace" in _msg()
+    assert lib.dsa_topk(ctypes.byref(dec), FAKE, 131072, FAKE, FAKE + 8, need, None) == \
+        binding.DSA_ERR_INVALID_ARGUMENT
+    assert "aligned" in _msg()
+    fwd = lib.dsa_workspace_bytes(ctypes.byref(dec), binding.WS_FORWARD)
+    assert fwd >= need + 64 * 131072 * 4
+
+
 def test_forward_needs_its_workspace():
     lib = binding.load_library()
     p = _problem()

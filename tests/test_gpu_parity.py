@@ -70,8 +70,12 @@ def test_indexer_decode_batch_ragged():
 
 
 # ---------------------------------------------------------------- top-k
-def _topk_on(scores_rows, lengths, k):
-    """Run dsa_topk on explicit score rows (decode layout: one row per sequence)."""
+def _topk_on(scores_rows, lengths, k, pad_rows=0):
+    """Run dsa_topk on explicit score rows (decode layout: one row per sequence).
+    Small batches cut long rows into segments over several workgroups; with
+    `pad_rows` extra one-score sequences the batch is large enough for the
+    one-workgroup-per-row kernel instead."""
+    lengths = list(lengths) + [1] * pad_rows
     B = len(lengths)
     ld = max(64, (max(lengths) + 63) // 64 * 64)
     sc = torch.zeros(B, ld, dtype=torch.float32)
@@ -85,7 +89,9 @@ def _topk_on(scores_rows, lengths, k):
                        d_latent=64, d_rope=16, topk=k, softmax_scale=0.1)
     sc_d = sc.cuda()
     idx = torch.full((B, k), -7, dtype=torch.int32, device="cuda")
-    dsa.topk(prob, sc_d, idx, ld=ld)
+    nws = dsa.workspace_bytes(prob, dsa.WS_TOPK)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda") if nws else None
+    dsa.topk(prob, sc_d, idx, ld=ld, workspace=ws)
     torch.cuda.synchronize()
     return sc_d, idx
 
@@ -97,8 +103,9 @@ def test_topk_lengths_around_k_and_paths(k):
     lengths = sorted({1, 2, max(1, k - 1), k, k + 1, k + 37, 3 * k + 5, 12288, 12289, 40000,
                       131072})
     rows = [rng.standard_normal(n).astype(np.float32) * 32 + 144 for n in lengths]
-    sc, idx = _topk_on(rows, lengths, k)
-    H.check_topk_rows(idx, sc, list(range(len(lengths))), lengths, k)
+    for pad in (0, 600):     # row segments over workgroups, then one workgroup per row
+        sc, idx = _topk_on(rows, lengths, k, pad_rows=pad)
+        H.check_topk_rows(idx, sc, list(range(len(lengths))), lengths, k)
 
 
 def test_topk_ties_signed_zeros_and_fallbacks():
@@ -116,8 +123,20 @@ def test_topk_ties_signed_zeros_and_fallbacks():
         np.arange(20000, dtype=np.float32),                                 # sorted ascending
     ]
     lengths = [len(r) for r in rows]
+    for pad in (0, 600):
+        sc, idx = _topk_on(rows, lengths, k, pad_rows=pad)
+        H.check_topk_rows(idx, sc, list(range(len(rows))), lengths, k)
+
+
+def test_topk_rows_longer_than_32_segments():
+    """Rows long enough that each segment spans several filter steps."""
+    _announce("top-k rows of 270001 and 300000 scores, k=2048")
+    k = 2048
+    rng = np.random.default_rng(11)
+    lengths = [300000, 270001, 5000, 2048, 9000]
+    rows = [rng.standard_normal(n).astype(np.float32) * 32 + 144 for n in lengths]
     sc, idx = _topk_on(rows, lengths, k)
-    H.check_topk_rows(idx, sc, list(range(len(rows))), lengths, k)
+    H.check_topk_rows(idx, sc, list(range(len(lengths))), lengths, k)
 
 
 def test_topk_on_indexer_scores_prefill():
