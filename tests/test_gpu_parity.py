@@ -57,16 +57,40 @@ def test_indexer_chunk_against_causal_prefix():
     H.check_indexer_rows(scores, refs, np.arange(r1 - r0))
 
 
-def test_indexer_decode_batch_ragged():
-    wl = wk.DECODE_B64.scaled(decode_batch=6, ctx_min=100, ctx_max=3000)
-    _announce("indexer decode B=6 ctx 100..3000")
+@pytest.mark.parametrize("batch,ctx_min,ctx_max", [(6, 100, 3000), (1100, 1, 300)])
+def test_indexer_decode_batch_ragged(batch, ctx_min, ctx_max):
+    """Decode batches, from a few long caches to many of one to 300 keys."""
+    wl = wk.DECODE_B64.scaled(decode_batch=batch, ctx_min=ctx_min, ctx_max=ctx_max)
+    _announce(f"indexer decode B={batch} ctx {ctx_min}..{ctx_max}")
     inp = wk.generate(wl)
     prob = dsa.Problem.from_workload(wl, inp)
     scores = H.run_indexer(prob, H.to_dev(inp))
     offs = inp["kv_offsets"]
-    for b in range(wl.decode_batch):
+    rows = range(batch) if batch <= 64 else sorted(set(np.linspace(0, batch - 1, 48).astype(int)))
+    for b in rows:
         refs = H.oracle_scores_for_rows(inp, slice(b, b + 1), offs[b], [inp["q_pos0"][b]])
         H.check_indexer_rows(scores, refs, [b])
+    # entries past the causal limit are never written
+    sc = scores.cpu()
+    for b in rows:
+        assert torch.isnan(sc[b, int(inp["q_pos0"][b]) + 1:]).all()
+
+
+@pytest.mark.parametrize("r0,r1", [(698, 700), (0, 2), (0, 1), (333, 335)])
+def test_indexer_two_query_rows(r0, r1):
+    """One or two query rows of a sequence (the decode kernel) against the causal prefix."""
+    wl = MED
+    _announce(f"indexer rows [{r0},{r1}) of L=700")
+    inp = wk.generate(wl)
+    sub = {k: (v[r0:r1] if k in ("q_fp8", "q_scale", "w", "q") else
+               v[:r1] if k in ("k_fp8", "k_scale", "kv") else v) for k, v in inp.items()}
+    prob = dsa.Problem.from_workload(wl, inp, q_rows=slice(r0, r1), q_pos0=r0)
+    scores = H.run_indexer(prob, H.to_dev(sub))
+    refs = H.oracle_scores_for_rows(inp, slice(r0, r1), 0, np.arange(r0, r1))
+    H.check_indexer_rows(scores, refs, np.arange(r1 - r0))
+    sc = scores.cpu()
+    for i in range(r1 - r0):
+        assert torch.isnan(sc[i, r0 + i + 1:]).all()
 
 
 # ---------------------------------------------------------------- top-k
