@@ -12,10 +12,10 @@
 // scores) is read once from HBM in the common case:
 //  1. n <= k: every position is selected.
 //  2. Otherwise, a lower bound T_lo on the k-th largest order key comes from
-//     2048 sampled scores (a 16-bit radix select over the sample; the lower
+//     4096 sampled scores (a 16-bit radix select over the sample; the lower
 //     edge of the bin holding the sample's rank-j key): the sample rank is
-//     the expected count above the k-th key plus three standard deviations,
-//     so the candidates number about k plus a margin.  For rows that fit the
+//     the expected count above the k-th key plus 4.5 standard deviations, so
+//     the candidates number about k plus a margin.  For rows that fit the
 //     candidate buffer (n <= kCap) T_lo is the minimum key, i.e. all.
 //  3. One streaming pass (two steps of four 16-byte loads per thread in
 //     flight) writes every (key, position) with key >= T_lo to an LDS
@@ -43,15 +43,20 @@ constexpr int kThreads = 512;
 constexpr int kWavesPerBlock = kThreads / 64;
 constexpr int kCap = 5632;               // candidate buffer entries (key + position); three
                                          // workgroups' LDS fit one CU
-constexpr int kSamples = 2048;           // 64 runs of 32 consecutive scores
-constexpr int kSampleRuns = 64;
+constexpr int kSamples = 4096;           // 128 runs of 32 consecutive scores
+constexpr int kSampleRuns = 128;
 constexpr int kVec = 4;                  // float4 loads per thread and filter step
 constexpr int kMaxSegs = 32;             // segments per row in the few-rows path
 constexpr int kSplitRows = 512;          // batches up to this many rows use that path
 
 struct TopkShared {
-  uint32_t keys[kCap];
-  uint32_t pos[kCap];
+  union {
+    struct {
+      uint32_t keys[kCap];
+      uint32_t pos[kCap];
+    };
+    uint32_t sample[kSamples];   // the sample phase only
+  };
   uint32_t hist[256];
   uint32_t scan[kWavesPerBlock];
   uint32_t scan2[kWavesPerBlock];
@@ -233,31 +238,47 @@ __device__ void select_from_global(const float *row, int64_t n, int k, int32_t *
   }
 }
 
-// Lower bound on the k-th largest key of a row with n > kCap scores, from
-// 2048 sampled scores (uniform over the workgroup; 0 when every score passes).
+// Lower bound on the k-th largest key of a row with n > kCap scores (uniform
+// over the workgroup; 0 when every score passes).  A row of at most kSamples
+// scores is read whole and the bound comes from its own k-th key.  A longer
+// row is sampled: S = kSamples scores in 128 runs of 32 consecutive ones
+// spread evenly over the row.  The bound is the sample's key of rank
+// j = E + 4.5 sqrt(E) + 4, where E = S k / n is the expected number of
+// sampled scores at or above the row's k-th key (sqrt(E) its Poisson
+// deviation): the bound exceeds that key only if j or more sampled scores
+// lie above it.  The bound sits near rank n j / S of the row, which is about
+// the number of candidates the filter then keeps.
 __device__ uint32_t sample_bound(const float *rowp, int64_t n, int k, TopkShared &sh) {
+  static_assert(kSamples % kThreads == 0 && kSamples <= 2 * kCap, "sample layout");
   uint32_t t_lo = 0u;
   if (n > kCap) {
     const int tid = (int)__builtin_amdgcn_workitem_id_x();
+    const bool whole = n <= kSamples;
+    const int count = whole ? (int)n : kSamples;
     const int64_t span = n - 32;
     constexpr int kPer = kSamples / kThreads;
     float v[kPer];   // all loads in flight before the first LDS store
 #pragma unroll
     for (int u = 0; u < kPer; ++u) {
       const int i = tid + u * kThreads, run = i >> 5, off = i & 31;
-      v[u] = rowp[span * run / (kSampleRuns - 1) + off];
+      const int64_t at = whole ? (i < n ? i : n - 1) : span * run / (kSampleRuns - 1) + off;
+      v[u] = rowp[at];
     }
 #pragma unroll
-    for (int u = 0; u < kPer; ++u) sh.keys[tid + u * kThreads] = order_key(v[u]);
+    for (int u = 0; u < kPer; ++u)
+      if (tid + u * kThreads < count) sh.sample[tid + u * kThreads] = order_key(v[u]);
     __syncthreads();
-    const double expect = (double)kSamples * (double)k / (double)n;
-    int64_t j = (int64_t)(expect + 3.0 * sqrt(expect) + 4.0);
-    if (j > kSamples) j = kSamples;
+    int64_t j = k;
+    if (!whole) {
+      const double expect = (double)kSamples * (double)k / (double)n;
+      j = (int64_t)(expect + 4.5 * sqrt(expect) + 4.0);
+      if (j > kSamples) j = kSamples;
+    }
     uint32_t n_above_s;
     // two radix passes (16 bits below the shared prefix) are enough: the
     // bin's lower edge is a valid lower bound, and a bin that narrow adds
     // few scores
-    radix_select([&](int64_t i) { return sh.keys[i]; }, kSamples, (uint32_t)j, sh, t_lo, n_above_s, 2);
+    radix_select([&](int64_t i) { return sh.sample[i]; }, count, (uint32_t)j, sh, t_lo, n_above_s, 2);
   }
   __syncthreads();
   return t_lo;
