@@ -119,7 +119,7 @@ __device__ __forceinline__ void build_linear_pieces(const IndexerArgs &p, const 
     const uint8_t *qrow = p.q_fp8 + row * H * d + (dim_ok ? dl : 0);
     const float *wrow = p.w + row * H;
     float e0 = 0.f, e1 = 0.f, e2 = 0.f, e3 = 0.f;
-#pragma unroll 16
+#pragma unroll 64
     for (int j = 0; j < H; ++j) {
       const uint32_t x = *reinterpret_cast<const uint32_t *>(qrow + (int64_t)j * d);
       const float wj = wrow[j];
@@ -203,9 +203,12 @@ void indexer_prefill_kernel(IndexerArgs p, int key_split) {
     valid[qi] = r < qlen;
     grow[qi] = s.q0 + (valid[qi] ? r : 0);
     pos[qi] = valid[qi] ? (int)row_pos(s, grow[qi]) : -1;
-    load_query<HB>(q[qi], p, grow[qi], valid[qi], g, c, 0.5f);
   }
+  // The linear operand first, while no query operand occupies registers: all
+  // of its loads can then be in flight at once.
   build_linear_pieces<QW>(p, grow, valid, lane, linq[wave], lininv[wave]);
+#pragma unroll
+  for (int qi = 0; qi < QW; ++qi) load_query<HB>(q[qi], p, grow[qi], valid[qi], g, c, 0.5f);
 
   // Each thread stages two 16-byte chunks of a 64-key tile (512 chunks).
   const int d = p.idx_dim;
