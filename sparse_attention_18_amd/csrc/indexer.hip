@@ -180,7 +180,13 @@ void indexer_prefill_kernel(IndexerArgs p, int key_split) {
   const int64_t rows_here = qlen - row_begin < QT ? qlen - row_begin : QT;
   const int64_t last_pos = row_pos(s, s.q0 + row_begin + rows_here - 1);
   // Positions inside one sequence fit in int32 (the offsets are int32).
-  const int key_begin = (int)__builtin_amdgcn_workgroup_id_x() * key_split;
+  // Workgroup x runs on XCD x % 8 (dispatch is round-robin over the eight
+  // XCDs, and the split count is a multiple of 8), so each XCD keeps a fixed
+  // set of key splits in its L2.  The splits go to the XCDs in snake order
+  // (x, 15 - x, 16 + x, 31 - x, ...): under the causal triangle later splits
+  // have less work, and the pairs even it out across the XCDs.
+  const int sx = (int)__builtin_amdgcn_workgroup_id_x(), sxcd = sx & 7, sj = sx >> 3;
+  const int key_begin = ((sj & 1) ? 8 * sj + 7 - sxcd : 8 * sj + sxcd) * key_split;
   if (key_begin > last_pos) return;
   const int key_end = key_begin + key_split < last_pos + 1 ? key_begin + key_split : (int)last_pos + 1;
   const int kvlen = (int)s.kvlen;
@@ -358,19 +364,24 @@ template <int HB, int QW>
 hipError_t launch_prefill(const IndexerArgs &a, hipStream_t stream) {
   constexpr int QT = kWaves * QW;
   const int64_t qtiles = (a.seq.max_q_len + QT - 1) / QT;
-  // Key split: the longest (256..4096 keys) that still leaves about 6K
-  // workgroups with work, i.e. several rounds of the 256 CUs x 2-3 resident
-  // workgroups, so that the causal tail evens out.  Longer splits re-load the
-  // queries and rebuild their linear operand less often.  Work estimate: the
-  // longest sequence's queries sit at its last max_q_len positions.
+  // Key splits: 8m of them, m >= 2, of equal length (a multiple of 64), so
+  // that every XCD gets the same share of the keys.  m is the smallest that
+  // leaves about 6K workgroups with work (several rounds of the 256 CUs x 2-3
+  // resident workgroups, so the causal tail evens out), with splits of at
+  // least 256 keys; fewer, longer splits load the queries and build their
+  // linear operand less often.  Work estimate: the longest sequence's queries
+  // sit at its last max_q_len positions.
   const double first_pos = (double)(a.seq.max_kv_len - a.seq.max_q_len);
   auto busy_blocks = [&](int64_t sp) {
     const double t = (double)qtiles;
     return ((t * first_pos + QT * t * (t + 1) / 2) / sp + t / 2) * a.seq.batch;
   };
-  int64_t split = 4096;
-  while (split > 256 && busy_blocks(split) < 6144) split /= 2;
-  const int64_t nsplit = ((a.seq.max_kv_len + split - 1) / split + 7) / 8 * 8;
+  const int64_t kv = a.seq.max_kv_len;
+  auto split_of = [&](int64_t m) { return ((kv + 8 * m - 1) / (8 * m) + 63) / 64 * 64; };
+  int64_t m = 2;
+  while (split_of(m + 1) >= 256 && busy_blocks(split_of(m)) < 6144) ++m;
+  const int64_t split = split_of(m);
+  const int64_t nsplit = 8 * m;
   dim3 grid((unsigned)nsplit, (unsigned)qtiles, (unsigned)a.seq.batch);
   hipLaunchKernelGGL((indexer_prefill_kernel<HB, QW>), grid, dim3(256), 0, stream, a, (int)split);
   return hipGetLastError();
