@@ -311,8 +311,8 @@ constexpr int kDecodeChunk = 1024;  // keys per workgroup (4 waves x 256)
 template <int HB>
 __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs p) {
   const int64_t row = __builtin_amdgcn_workgroup_id_y();
-  const int b = find_seq(p.seq, row);
-  const SeqInfo s = load_seq(p.seq, b);
+  SeqInfo s;
+  const int b = row_seq(p.seq, row, s);
   if (row < s.q0 || row >= s.q1 || s.kvlen <= 0) return;
   const int64_t pos = row_pos(s, row);
   const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63, wave = tid >> 6;
@@ -326,37 +326,63 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs p) {
   load_query<HB>(q, p, row, true, g, c, 1.0f);
   const int d = p.idx_dim;
 
-  auto load_b = [&](int64_t t0, int kb) {
-    const int64_t key = t0 + kb * 16 + c;
-    v4i lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
-    if (key < wave_end && 32 * g < d) {
-      const v4i *src = reinterpret_cast<const v4i *>(p.k_fp8 + (s.kv0 + key) * d + 32 * g);
-      lo = src[0];
-      hi = src[1];
-    }
-    return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  // Keys and key scales are read through buffer descriptors spanning this
+  // wave's slice: loads past it return zeros, so every load is issued
+  // unconditionally.  With no branch around them the compiler counts them,
+  // and the wait before a step's MFMAs covers only that step's loads; the
+  // next step's stay in flight.  Dims at or past d_I get an offset past the
+  // range (zeros too).  The scores go to LDS and are written out after the
+  // last load: a store between the loads would hold up the waits on them,
+  // which share one in-order counter.
+  __shared__ float s_sc[kWaves][kDecodeChunk / kWaves];
+  const int nk = __builtin_amdgcn_readfirstlane((int)(wave_end - wave_begin));   // 1..256 keys
+  auto rsrc = [&](const void *base, int bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    const uint64_t u = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a) |
+                       ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) << 32);
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)u, (short)0, bytes, 0x00020000);
   };
-
-  v8i cur[4], nxt[4];
+  const __amdgpu_buffer_rsrc_t krs = rsrc(p.k_fp8 + (s.kv0 + wave_begin) * d, nk * d);
+  const __amdgpu_buffer_rsrc_t srs = rsrc(p.k_scale + s.kv0 + wave_begin, nk * 4);
+  const int koff = 32 * g < d ? c * d + 32 * g : 0x40000000;
+  auto load_step = [&](int st, v8i (&kr)[4], float &ks) {
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) cur[kb] = load_b(wave_begin, kb);
-  for (int64_t t0 = wave_begin; t0 < wave_end; t0 += 64) {
-    const bool has_next = t0 + 64 < wave_end;
-    if (has_next) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) nxt[kb] = load_b(t0 + 64, kb);
+    for (int kb = 0; kb < 4; ++kb) {
+      const int so = (st * 64 + kb * 16) * d;
+      const v4i lo = __builtin_amdgcn_raw_buffer_load_b128(krs, koff, so, 0);
+      const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(krs, koff + 16, so, 0);
+      kr[kb] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
-    const int64_t my_key = t0 + lane;
-    const float ks = my_key < wave_end ? p.k_scale[s.kv0 + my_key] : 0.f;
+    ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, lane * 4, st * 256, 0));
+  };
+  auto score_step = [&](int st, const v8i (&kr)[4], float ks) {
     float part[4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) part[kb] = score_block<HB, false>(q, cur[kb], 0.f);
-    const float v = reduce_four_blocks(part[0], part[1], part[2], part[3]);
-    if (my_key < wave_end) p.scores[row * p.ld + my_key] = v * ks;
-    if (has_next) {
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) cur[kb] = nxt[kb];
+    for (int kb = 0; kb < 4; ++kb) part[kb] = score_block<HB, false>(q, kr[kb], 0.f);
+    s_sc[wave][st * 64 + lane] = reduce_four_blocks(part[0], part[1], part[2], part[3]) * ks;
+  };
+  // Two register sets take turns (no copy of a set whose loads are still in
+  // flight, which would wait for them); loads past the slice read zeros.
+  const int nsteps = (nk + 63) / 64;
+  v8i ka[4], kb2[4];
+  float ksa, ksb;
+  // (The scheduling barriers keep each set's loads ahead of the other set's
+  // MFMAs.)
+  load_step(0, ka, ksa);
+  for (int st = 0; st < nsteps; st += 2) {
+    load_step(st + 1, kb2, ksb);
+    __builtin_amdgcn_sched_barrier(0);
+    score_step(st, ka, ksa);
+    if (st + 1 < nsteps) {
+      load_step(st + 2, ka, ksa);
+      __builtin_amdgcn_sched_barrier(0);
+      score_step(st + 1, kb2, ksb);
     }
+  }
+  float *srow = p.scores + row * p.ld;
+  for (int64_t t0 = wave_begin; t0 < wave_end; t0 += 64) {
+    const int64_t my_key = t0 + lane;
+    if (my_key < wave_end) srow[my_key] = s_sc[wave][t0 - wave_begin + lane];
   }
 }
 

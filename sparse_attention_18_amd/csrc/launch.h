@@ -69,17 +69,15 @@ struct SeqInfo {
   int64_t pos0;      // position of row q0
 };
 
-__device__ __forceinline__ SeqInfo load_seq(const SeqLayout &L, int b) {
+__device__ __forceinline__ SeqInfo clamp_seq(const SeqLayout &L, int64_t q0, int64_t q1, int64_t k0,
+                                             int64_t k1, int64_t p0) {
   SeqInfo s;
-  int64_t q0 = L.q_offsets[b], q1 = L.q_offsets[b + 1];
-  int64_t k0 = L.kv_offsets[b], k1 = L.kv_offsets[b + 1];
   q0 = q0 < 0 ? 0 : (q0 > L.total_q ? L.total_q : q0);
   q1 = q1 < q0 ? q0 : (q1 > L.total_q ? L.total_q : q1);
   k0 = k0 < 0 ? 0 : (k0 > L.total_kv ? L.total_kv : k0);
   k1 = k1 < k0 ? k0 : (k1 > L.total_kv ? L.total_kv : k1);
   int64_t kvlen = k1 - k0;
   if (kvlen > L.max_kv_len) kvlen = L.max_kv_len;
-  int64_t p0 = L.q_pos0[b];
   p0 = p0 < 0 ? 0 : p0;
   s.q0 = q0;
   s.q1 = q1;
@@ -87,6 +85,10 @@ __device__ __forceinline__ SeqInfo load_seq(const SeqLayout &L, int b) {
   s.kvlen = kvlen;
   s.pos0 = p0;
   return s;
+}
+
+__device__ __forceinline__ SeqInfo load_seq(const SeqLayout &L, int b) {
+  return clamp_seq(L, L.q_offsets[b], L.q_offsets[b + 1], L.kv_offsets[b], L.kv_offsets[b + 1], L.q_pos0[b]);
 }
 
 // Position of packed query row r in sequence s, clamped into [0, kvlen-1]
@@ -112,6 +114,24 @@ __device__ __forceinline__ int find_seq(const SeqLayout &L, int64_t r) {
     cnt += __popcll(__ballot(le));
   }
   return cnt > 0 ? cnt - 1 : 0;
+}
+
+// Sequence of packed query row r and its metadata.  Decode batches hold one
+// query row per sequence (row r is sequence r); that layout is checked on
+// loads issued together with the general search, so there the metadata
+// arrives in one memory round trip instead of two.  r must be uniform across
+// the wave and every lane active.
+__device__ __forceinline__ int row_seq(const SeqLayout &L, int64_t r, SeqInfo &s) {
+  const int rr = (int)(r < L.batch ? r : L.batch - 1);
+  const int64_t q0 = L.q_offsets[rr], q1 = L.q_offsets[rr + 1];
+  const int64_t k0 = L.kv_offsets[rr], k1 = L.kv_offsets[rr + 1], p0 = L.q_pos0[rr];
+  if (r < L.batch && q0 == r && q1 == r + 1) {
+    s = clamp_seq(L, q0, q1, k0, k1, p0);
+    return rr;
+  }
+  const int b = find_seq(L, r);
+  s = load_seq(L, b);
+  return b;
 }
 
 }  // namespace dsa

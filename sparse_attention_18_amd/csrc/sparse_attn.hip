@@ -182,8 +182,8 @@ void mla_sparse_attn_kernel(AttnArgs p) {
       qb[kk] = as_v8bf(*reinterpret_cast<const v4i *>(qrow + 16 * kk));
   }
 
-  const int b = find_seq(p.seq, t);
-  const SeqInfo s = load_seq(p.seq, b);
+  SeqInfo s;
+  const int b = row_seq(p.seq, t, s);
   const bool row_ok = t >= s.q0 && t < s.q1;
 
   // Compact the row's valid indices (in order) into idxl; m = their count.
@@ -486,8 +486,8 @@ __global__ __launch_bounds__(128) void combine_splits_kernel(AttnArgs p, int hea
   const int64_t th = __builtin_amdgcn_workgroup_id_x();     // token * heads + head
   const int tid = (int)__builtin_amdgcn_workitem_id_x();
   const int64_t t = th / heads;
-  const int b = find_seq(p.seq, t);
-  const SeqInfo s = load_seq(p.seq, b);
+  SeqInfo s;
+  const int b = row_seq(p.seq, t, s);
   if (t < s.q0 || t >= s.q1) return;
   const int S = p.nsplit;
   const int64_t per_split = p.seq.total_q * heads;
@@ -526,8 +526,8 @@ __global__ __launch_bounds__(kSmallThreads) void small_sparse_attn_kernel(AttnAr
   __shared__ int rows[kSmallMaxK];
   __shared__ float red[kSmallThreads / 64];
   const int64_t t = blockIdx.x;
-  const int b = find_seq(p.seq, t);
-  const SeqInfo s = load_seq(p.seq, b);
+  SeqInfo s;
+  const int b = row_seq(p.seq, t, s);
   if (t < s.q0 || t >= s.q1) return;
   const int H = p.heads, D = p.d_latent + p.d_rope, DL = p.d_latent, k = p.k;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;

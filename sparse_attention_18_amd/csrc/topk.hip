@@ -433,8 +433,8 @@ __global__ __launch_bounds__(kThreads)
 void topk_kernel(TopkArgs p) {
   __shared__ TopkShared sh;
   const int64_t row = __builtin_amdgcn_workgroup_id_x();
-  const int b = find_seq(p.seq, row);
-  const SeqInfo s = load_seq(p.seq, b);
+  SeqInfo s;
+  const int b = row_seq(p.seq, row, s);
   int32_t *out = p.idx + row * p.k;
   if (row < s.q0 || row >= s.q1 || s.kvlen <= 0) {
     emit_all(out, 0, p.k);
@@ -478,8 +478,8 @@ void topk_segment_kernel(TopkArgs p, uint32_t *counts, uint2 *cands) {
   __shared__ TopkShared sh;
   const int64_t row = __builtin_amdgcn_workgroup_id_y();
   const int seg = __builtin_amdgcn_workgroup_id_x();
-  const int b = find_seq(p.seq, row);
-  const SeqInfo s = load_seq(p.seq, b);
+  SeqInfo s;
+  const int b = row_seq(p.seq, row, s);
   if (row < s.q0 || row >= s.q1 || s.kvlen <= 0) return;
   const int64_t n = row_pos(s, row) + 1;
   const int k = p.k;
@@ -502,8 +502,8 @@ __global__ __launch_bounds__(kThreads)
 void topk_merge_kernel(TopkArgs p, const uint32_t *counts, const uint2 *cands) {
   __shared__ TopkShared sh;
   const int64_t row = __builtin_amdgcn_workgroup_id_x();
-  const int b = find_seq(p.seq, row);
-  const SeqInfo s = load_seq(p.seq, b);
+  SeqInfo s;
+  const int b = row_seq(p.seq, row, s);
   int32_t *out = p.idx + row * p.k;
   if (row < s.q0 || row >= s.q1 || s.kvlen <= 0) {
     emit_all(out, 0, p.k);
