@@ -63,6 +63,7 @@ constexpr int kMaxK = 4096;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kFrameSlack = 32.f;          // log2 headroom above the frame max
+constexpr int kMaxSplits = 4;                // workgroups per token in the split path
 static_assert(kBN * kChunks % 64 == 0, "tile must be whole 1 KB loads");
 
 __device__ __forceinline__ v8bf as_v8bf(const v4i &x) { return __builtin_bit_cast(v8bf, x); }
@@ -489,22 +490,31 @@ __global__ __launch_bounds__(128) void combine_splits_kernel(AttnArgs p, int hea
   SeqInfo s;
   const int b = row_seq(p.seq, t, s);
   if (t < s.q0 || t >= s.q1) return;
-  const int S = p.nsplit;
+  const int S = p.nsplit;   // 2..kMaxSplits
   const int64_t per_split = p.seq.total_q * heads;
   const float *wo = reinterpret_cast<const float *>(p.workspace);
   const float2 *wml = reinterpret_cast<const float2 *>(wo + (int64_t)S * per_split * kDL);
+  // Every split's loads are issued before any is used (clamped to the last
+  // split past S, whose weight is then zero).
+  float2 ml[kMaxSplits];
+  v4f x[kMaxSplits];
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp) {
+    const int64_t at = (int64_t)(sp < S ? sp : S - 1) * per_split + th;
+    ml[sp] = wml[at];
+    x[sp] = *reinterpret_cast<const v4f *>(wo + at * kDL + 4 * tid);
+  }
   float M = -INFINITY;
-  for (int sp = 0; sp < S; ++sp) M = fmaxf(M, wml[sp * per_split + th].x);
+#pragma unroll
+  for (int sp = 0; sp < kMaxSplits; ++sp) M = fmaxf(M, ml[sp].x);
   v4f acc = {0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   if (M != -INFINITY) {
-    for (int sp = 0; sp < S; ++sp) {
-      const float2 ml = wml[sp * per_split + th];
-      if (ml.x == -INFINITY) continue;
-      const float e = __builtin_amdgcn_exp2f(ml.x - M);
-      L = fmaf(e, ml.y, L);
-      const v4f x = *reinterpret_cast<const v4f *>(wo + (sp * per_split + th) * kDL + 4 * tid);
-      acc = acc + e * x;
+#pragma unroll
+    for (int sp = 0; sp < kMaxSplits; ++sp) {
+      const float e = (sp < S && ml[sp].x != -INFINITY) ? __builtin_amdgcn_exp2f(ml[sp].x - M) : 0.f;
+      L = fmaf(e, ml[sp].y, L);
+      acc = acc + e * x[sp];
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -588,11 +598,12 @@ bool mfma_shape(const AttnArgs &a) {
          (a.heads == 32 || a.heads == 64 || a.heads == 128);
 }
 
-// Workgroups per token: enough that a small batch still covers the 256 CUs.
+// Workgroups per token: enough that a small batch still covers the 256 CUs
+// (at most kMaxSplits).
 int attn_splits(const AttnArgs &a) {
   if (!mfma_shape(a) || a.seq.total_q == 0) return 1;
   const int64_t s = 256 / a.seq.total_q;
-  return s >= 4 ? 4 : (s >= 2 ? 2 : 1);
+  return s >= kMaxSplits ? kMaxSplits : (s >= 2 ? 2 : 1);
 }
 
 }  // namespace
