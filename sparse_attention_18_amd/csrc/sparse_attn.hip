@@ -346,11 +346,12 @@ void mla_sparse_attn_kernel(AttnArgs p) {
 
     // ---- softmax of tile tq: scale + mask + max, frame update, exp2 + sum
     // + bf16, publish P^T into pbuf[tq & 1].
+    // The logits stay unscaled until the exponent: scale * log2(e) > 0, so
+    // the maximum of the raw values times it is the scaled maximum, and the
+    // scaling rides on the FMA that forms the exponent's argument.
     auto sm_scale = [&](v16f &sc, int tq, int j0, int j1, float &mt) {
       const int valid_rows = nrows - tq * kBN;   // >= 1
       const bool partial = valid_rows < kBN; // only the last tile can be partial
-#pragma unroll
-      for (int jj = j0; jj < j1; ++jj) sc[jj] *= sl2;
       if (partial) {
         const int vr = valid_rows - 4 * G;      // element jj is row 8(jj/4) + 4G + jj%4
 #pragma unroll
@@ -361,20 +362,22 @@ void mla_sparse_attn_kernel(AttnArgs p) {
       for (int jj = j0; jj < j1; ++jj) mt = fmaxf(mt, sc[jj]);
     };
     auto sm_frame = [&](float mt) {
-      mt = max_across_halves(mt);
+      mt = max_across_halves(mt) * sl2;
       m_seen = fmaxf(m_seen, mt);
       if (m_used == -INFINITY) m_used = mt;          // first tile
       overflow |= mt > m_used + kFrameSlack;
     };
     auto sm_exp = [&](const v16f &sc, v8bf (&pb)[2], int j0, int j1) {
+      float ls[4] = {0.f, 0.f, 0.f, 0.f};   // four short sum chains instead of one long one
 #pragma unroll
       for (int jj = j0; jj < j1; ++jj) {
         // raw v_exp_f32: arguments below -126 flush to 0, which a softmax
         // weight that small is anyway next to the frame maximum's 1.0
-        const float pe = __builtin_amdgcn_exp2f(sc[jj] - m_used);
-        l_part += pe;
+        const float pe = __builtin_amdgcn_exp2f(fmaf(sc[jj], sl2, -m_used));
+        ls[jj & 3] += pe;
         pb[jj >> 3][jj & 7] = (__bf16)pe;
       }
+      l_part += (ls[0] + ls[1]) + (ls[2] + ls[3]);
     };
     auto sm_store = [&](const v8bf (&pb)[2], int tq) {
       uint8_t *pw = pbuf[tq & 1];
