@@ -7,7 +7,8 @@ selector and the sparse MLA attention against its full causal prefix
 ``value`` is prefill tokens/s over the K timed steps, with every input
 already resident in HBM.  The same run also times the decode step (64
 sequences, cached contexts uniform in [8K, 128K]) and reports it as
-``decode_us_per_step``.
+``decode_us_per_step``, and the same decode step over paged caches (64-row
+blocks, shuffled) as ``decode_paged_us_per_step``.
 
 Per-stage durations come from HIP events recorded around each stage call on
 the stream the kernels run on.  ``roofline`` covers the dominant stage:
@@ -235,7 +236,27 @@ def run_decode(args, dev):
     torch.cuda.synchronize()
     us = a.elapsed_time(b) * 1e3 / n
     log(f"[bench] decode step {us:.1f} us")
-    return us, inp
+
+    # The same step over paged caches (64-row blocks, shuffled).
+    table, nblocks, kc, ksc, kvc = wk.paged_caches(inp, 64, seed=1, device=dev)
+    pg = dsa.PagedKV(table, 64, nblocks, device=dev)
+
+    def step_paged():
+        dsa.forward_paged(prob, pg, inp["q_fp8"], inp["q_scale"], inp["w"], kc, ksc, inp["q"], kvc,
+                          out, lse, idx, ws)
+
+    for _ in range(3):
+        step_paged()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(n):
+        step_paged()
+    b.record()
+    torch.cuda.synchronize()
+    us_paged = a.elapsed_time(b) * 1e3 / n
+    log(f"[bench] decode step over paged caches {us_paged:.1f} us")
+    del kc, ksc, kvc
+    return us, us_paged, inp
 
 
 def cpu_baseline(bench, wl, rows_n):
@@ -311,9 +332,9 @@ def main():
     roofline = {"bound": d["bound"], "achieved": d["achieved"], "peak": d["peak"],
                 "unit": d["unit"], "frac": d["frac"], "traffic": traffic, "kernel": dominant,
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)"}
-    decode_us = None
+    decode_us = decode_paged_us = None
     if not args.no_decode:
-        decode_us, _ = run_decode(args, dev)
+        decode_us, decode_paged_us, _ = run_decode(args, dev)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(bench, wl, args.cpu_rows)
@@ -330,6 +351,7 @@ def main():
                    "heads": wl.heads, "d_qk": wl.d_qk, "d_latent": wl.d_latent,
                    "parallelism": "single GPU"},
         "decode_us_per_step": None if decode_us is None else round(decode_us, 1),
+        "decode_paged_us_per_step": None if decode_paged_us is None else round(decode_paged_us, 1),
         "decode_config": {"workload": wk.DECODE_B64.name, "batch": 64,
                           "ctx": [wk.DECODE_B64.ctx_min, wk.DECODE_B64.ctx_max]},
         "roofline": roofline,

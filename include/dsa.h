@@ -157,9 +157,54 @@ dsa_status dsa_forward(const dsa_problem *p, const uint8_t *q_fp8, const float *
                        int32_t *topk_idx_out, void *workspace, size_t workspace_bytes,
                        void *stream);
 
+/*
+ * Paged caches (a serving layout: the FP8 indexer-key cache and the latent KV
+ * cache of the decode setting are kept in fixed-size blocks, as the vLLM and
+ * SGLang backends the ivugangingo.com article names in "Sparse attention with
+ * almost linear long-context costs" do; the pages give no layout, so this one
+ * is this library's).  Key position s of sequence b lives in physical block
+ * block_table[b * max_blocks + s / block_size], at slot s % block_size:
+ *   k_cache  [num_blocks, block_size, d_I] uint8     (e4m3fn)
+ *   ks_cache [num_blocks, block_size] float          (per-row key scale)
+ *   kv_cache [num_blocks, block_size, d_latent + d_rope] bf16
+ * The problem's kv_offsets still give each sequence's length (kv_len_b =
+ * kv_offsets[b+1] - kv_offsets[b]); rows are found through the table only.
+ * Requirements: block_size a power of two >= 64; max_blocks * block_size >=
+ * max_kv_len; num_blocks * block_size < 2^31.  Table entries are clamped to
+ * [0, num_blocks), so a bad table gives wrong results but no out-of-bounds
+ * access.  The table is a device array of batch * max_blocks int32.
+ */
+typedef struct dsa_paged_kv {
+  const int32_t *block_table; /* device [batch, max_blocks]                        */
+  int32_t block_size;         /* key rows per block, a power of two >= 64          */
+  int32_t max_blocks;         /* row stride of block_table                         */
+  int64_t num_blocks;         /* physical blocks in each cache                     */
+} dsa_paged_kv;
+
+/* dsa_indexer_scores over paged key caches: the same scores, with key
+ * position s of sequence b read from k_cache / ks_cache through the table. */
+dsa_status dsa_indexer_scores_paged(const dsa_problem *p, const dsa_paged_kv *pg,
+                                    const uint8_t *q_fp8, const float *q_scale, const float *w,
+                                    const uint8_t *k_cache, const float *ks_cache, float *scores,
+                                    int64_t ld_scores, void *stream);
+
+/* dsa_sparse_attn over a paged latent KV cache (selected positions are
+ * translated through the table).  Workspace as for dsa_sparse_attn. */
+dsa_status dsa_sparse_attn_paged(const dsa_problem *p, const dsa_paged_kv *pg, const uint16_t *q,
+                                 const uint16_t *kv_cache, const int32_t *topk_idx, uint16_t *out,
+                                 float *lse, void *workspace, size_t workspace_bytes, void *stream);
+
+/* dsa_forward over paged caches.  Workspace as for dsa_forward. */
+dsa_status dsa_forward_paged(const dsa_problem *p, const dsa_paged_kv *pg, const uint8_t *q_fp8,
+                             const float *q_scale, const float *w, const uint8_t *k_cache,
+                             const float *ks_cache, const uint16_t *q, const uint16_t *kv_cache,
+                             uint16_t *out, float *lse, int32_t *topk_idx_out, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
 /* Bytes of device workspace the given entry point needs for problem p
  * (which = DSA_WS_TOPK, DSA_WS_ATTN or DSA_WS_FORWARD); 0 if none.  Returns
- * (size_t)-1 for an invalid problem (see dsa_last_error). */
+ * (size_t)-1 for an invalid problem (see dsa_last_error).  The paged entry
+ * points need the same amounts. */
 size_t dsa_workspace_bytes(const dsa_problem *p, int which);
 
 /* Message for the last non-OK status returned on this thread ("" if none). */

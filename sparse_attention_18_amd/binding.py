@@ -26,6 +26,7 @@ DSA_ERR_HIP = 4
 WS_TOPK, WS_ATTN, WS_FORWARD = 0, 1, 2
 
 EXPORTED = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward",
+            "dsa_indexer_scores_paged", "dsa_sparse_attn_paged", "dsa_forward_paged",
             "dsa_workspace_bytes", "dsa_last_error", "dsa_version")
 
 
@@ -63,6 +64,17 @@ class DsaProblem(ctypes.Structure):
     ]
 
 
+class DsaPagedKV(ctypes.Structure):
+    """Mirror of ``dsa_paged_kv`` in include/dsa.h."""
+
+    _fields_ = [
+        ("block_table", ctypes.c_void_p),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int64),
+    ]
+
+
 def library_path() -> str:
     return _LIB_PATH
 
@@ -86,7 +98,12 @@ def load_library():
         lib.dsa_topk.argtypes = [P, vp, i64, vp, vp, sz, vp]
         lib.dsa_sparse_attn.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.dsa_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-        for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward"):
+        G = ctypes.POINTER(DsaPagedKV)
+        lib.dsa_indexer_scores_paged.argtypes = [P, G, vp, vp, vp, vp, vp, vp, i64, vp]
+        lib.dsa_sparse_attn_paged.argtypes = [P, G, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.dsa_forward_paged.argtypes = [P, G, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward",
+                     "dsa_indexer_scores_paged", "dsa_sparse_attn_paged", "dsa_forward_paged"):
             getattr(lib, name).restype = ctypes.c_int
         lib.dsa_workspace_bytes.argtypes = [P, ctypes.c_int]
         lib.dsa_workspace_bytes.restype = sz
@@ -253,6 +270,83 @@ def forward(prob: Problem, q_fp8, q_scale, w, k_fp8, k_scale, q, kv, out, lse=No
         _ptr(k_scale, torch.float32, "k_scale", (c.total_kv,)),
         _ptr(q, torch.bfloat16, "q", (c.total_q, c.heads, D)),
         _ptr(kv, torch.bfloat16, "kv", (c.total_kv, D)),
+        _ptr(out, torch.bfloat16, "out", (c.total_q, c.heads, c.d_latent)),
+        _ptr(lse, torch.float32, "lse", (c.total_q, c.heads)),
+        _ptr(idx_out, torch.int32, "idx_out", (c.total_q, c.topk)),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
+
+
+class PagedKV:
+    """A ``dsa_paged_kv`` with its device block table kept alive.
+
+    ``block_table`` is a [batch, max_blocks] int32 tensor (any device; copied to
+    ``device``); ``num_blocks`` is the number of physical blocks in the caches."""
+
+    def __init__(self, block_table, block_size: int, num_blocks: int, device="cuda"):
+        bt = torch.as_tensor(block_table, dtype=torch.int32)
+        if bt.dim() != 2:
+            raise ValueError("block_table must be [batch, max_blocks]")
+        self.table = bt.to(device).contiguous()
+        self.block_size = int(block_size)
+        self.num_blocks = int(num_blocks)
+        self.c = DsaPagedKV(block_table=self.table.data_ptr(), block_size=self.block_size,
+                            max_blocks=int(bt.shape[1]), num_blocks=self.num_blocks)
+
+
+def _cache_shapes(c, pg: PagedKV):
+    nb, bs = pg.num_blocks, pg.block_size
+    return (nb, bs, c.idx_dim), (nb, bs), (nb, bs, c.d_latent + c.d_rope)
+
+
+def indexer_scores_paged(prob: Problem, pg: PagedKV, q_fp8, q_scale, w, k_cache, ks_cache, scores,
+                         ld=None, stream=None):
+    """dsa_indexer_scores_paged: the indexer with keys read through the block table."""
+    c = prob.c
+    ld = prob.ld_scores() if ld is None else int(ld)
+    ksh, ssh, _ = _cache_shapes(c, pg)
+    _check(load_library().dsa_indexer_scores_paged(
+        ctypes.byref(c), ctypes.byref(pg.c),
+        _ptr(q_fp8, torch.uint8, "q_fp8", (c.total_q, c.idx_heads, c.idx_dim)),
+        _ptr(q_scale, torch.float32, "q_scale", (c.total_q,)),
+        _ptr(w, torch.float32, "w", (c.total_q, c.idx_heads)),
+        _ptr(k_cache, torch.uint8, "k_cache", ksh),
+        _ptr(ks_cache, torch.float32, "ks_cache", ssh),
+        _ptr(scores, torch.float32, "scores", (c.total_q, ld)), ld, _stream(stream)))
+
+
+def sparse_attn_paged(prob: Problem, pg: PagedKV, q, kv_cache, idx, out, lse=None, workspace=None,
+                      stream=None):
+    """dsa_sparse_attn_paged: attention over latent rows read through the block table."""
+    c = prob.c
+    D = c.d_latent + c.d_rope
+    _, _, vsh = _cache_shapes(c, pg)
+    ws_ptr = _ptr(workspace, torch.uint8, "workspace") if workspace is not None else None
+    ws_n = workspace.numel() if workspace is not None else 0
+    _check(load_library().dsa_sparse_attn_paged(
+        ctypes.byref(c), ctypes.byref(pg.c), _ptr(q, torch.bfloat16, "q", (c.total_q, c.heads, D)),
+        _ptr(kv_cache, torch.bfloat16, "kv_cache", vsh),
+        _ptr(idx, torch.int32, "idx", (c.total_q, c.topk)),
+        _ptr(out, torch.bfloat16, "out", (c.total_q, c.heads, c.d_latent)),
+        _ptr(lse, torch.float32, "lse", (c.total_q, c.heads)), ws_ptr, ws_n, _stream(stream)))
+
+
+def forward_paged(prob: Problem, pg: PagedKV, q_fp8, q_scale, w, k_cache, ks_cache, q, kv_cache, out,
+                  lse=None, idx_out=None, workspace=None, stream=None):
+    """dsa_forward_paged: the three stages over paged caches."""
+    c = prob.c
+    D = c.d_latent + c.d_rope
+    if workspace is None:
+        raise ValueError("forward_paged needs a workspace tensor")
+    ksh, ssh, vsh = _cache_shapes(c, pg)
+    _check(load_library().dsa_forward_paged(
+        ctypes.byref(c), ctypes.byref(pg.c),
+        _ptr(q_fp8, torch.uint8, "q_fp8", (c.total_q, c.idx_heads, c.idx_dim)),
+        _ptr(q_scale, torch.float32, "q_scale", (c.total_q,)),
+        _ptr(w, torch.float32, "w", (c.total_q, c.idx_heads)),
+        _ptr(k_cache, torch.uint8, "k_cache", ksh),
+        _ptr(ks_cache, torch.float32, "ks_cache", ssh),
+        _ptr(q, torch.bfloat16, "q", (c.total_q, c.heads, D)),
+        _ptr(kv_cache, torch.bfloat16, "kv_cache", vsh),
         _ptr(out, torch.bfloat16, "out", (c.total_q, c.heads, c.d_latent)),
         _ptr(lse, torch.float32, "lse", (c.total_q, c.heads)),
         _ptr(idx_out, torch.int32, "idx_out", (c.total_q, c.topk)),

@@ -70,15 +70,16 @@ bool mfma_attn_shape(const dsa_problem *p) {
          (p->heads == 32 || p->heads == 64 || p->heads == 128);
 }
 
-dsa_status check_attn_dims(const dsa_problem *p) {
+dsa_status check_attn_dims(const dsa_problem *p, bool paged = false) {
   DSA_CHECK(p->heads >= 1, DSA_ERR_INVALID_ARGUMENT, "heads must be >= 1");
   DSA_CHECK(p->heads <= 128, DSA_ERR_UNSUPPORTED, "heads must be <= 128 (got %d)", p->heads);
   DSA_CHECK(p->d_latent >= 1 && p->d_rope >= 0, DSA_ERR_INVALID_ARGUMENT,
             "d_latent must be >= 1 and d_rope >= 0");
   DSA_CHECK(mfma_attn_shape(p) || p->d_latent + p->d_rope <= 1024, DSA_ERR_UNSUPPORTED,
             "d_latent + d_rope must be <= 1024 outside the (512, 64) MFMA shape");
-  // The MFMA path addresses a sequence's rows with 32-bit byte offsets.
-  DSA_CHECK(!mfma_attn_shape(p) || p->max_kv_len <= (int64_t)(UINT32_MAX / 1152u), DSA_ERR_UNSUPPORTED,
+  // The MFMA path addresses a sequence's rows with 32-bit byte offsets (the
+  // paged path with 64-bit addresses).
+  DSA_CHECK(paged || !mfma_attn_shape(p) || p->max_kv_len <= (int64_t)(UINT32_MAX / 1152u), DSA_ERR_UNSUPPORTED,
             "max_kv_len must be <= %u for the (512, 64) attention shape (got %lld)",
             (unsigned)(UINT32_MAX / 1152u), (long long)p->max_kv_len);
   DSA_CHECK(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f, DSA_ERR_INVALID_ARGUMENT,
@@ -94,6 +95,36 @@ dsa_status check_ld(const dsa_problem *p, int64_t ld) {
   DSA_CHECK(p->total_q == 0 || ld <= INT64_MAX / 4 / p->total_q, DSA_ERR_INVALID_ARGUMENT,
             "scores matrix size overflows");
   return DSA_OK;
+}
+
+// A paged-cache description consistent with the problem.
+dsa_status check_paged(const dsa_problem *p, const dsa_paged_kv *pg) {
+  DSA_CHECK(pg != nullptr, DSA_ERR_INVALID_ARGUMENT, "paged-cache description is NULL");
+  DSA_CHECK(pg->block_table != nullptr && aligned4(pg->block_table), DSA_ERR_INVALID_ARGUMENT,
+            "block_table must be a non-NULL, 4-byte aligned device array");
+  DSA_CHECK(pg->block_size >= 64 && (pg->block_size & (pg->block_size - 1)) == 0, DSA_ERR_UNSUPPORTED,
+            "block_size must be a power of two >= 64 (got %d)", pg->block_size);
+  DSA_CHECK(pg->max_blocks >= 1, DSA_ERR_INVALID_ARGUMENT, "max_blocks must be >= 1");
+  DSA_CHECK((int64_t)pg->max_blocks * pg->block_size >= p->max_kv_len, DSA_ERR_INVALID_ARGUMENT,
+            "max_blocks * block_size (%lld) must cover max_kv_len (%lld)",
+            (long long)pg->max_blocks * pg->block_size, (long long)p->max_kv_len);
+  DSA_CHECK(pg->num_blocks >= 1, DSA_ERR_INVALID_ARGUMENT, "num_blocks must be >= 1");
+  DSA_CHECK(p->max_kv_len <= INT32_MAX, DSA_ERR_UNSUPPORTED, "max_kv_len must fit int32");
+  DSA_CHECK(pg->num_blocks <= INT32_MAX / pg->block_size, DSA_ERR_UNSUPPORTED,
+            "num_blocks * block_size must be below 2^31");
+  DSA_CHECK((int64_t)p->batch * pg->max_blocks <= INT32_MAX, DSA_ERR_UNSUPPORTED,
+            "batch * max_blocks must fit int32");
+  return DSA_OK;
+}
+
+dsa::PagedKV paged_of(const dsa_paged_kv *pg) {
+  dsa::PagedKV k;
+  k.table = pg ? pg->block_table : nullptr;
+  k.block_shift = 0;
+  if (pg) while ((1 << k.block_shift) < pg->block_size) ++k.block_shift;
+  k.max_blocks = pg ? pg->max_blocks : 0;
+  k.num_blocks = pg ? (int32_t)pg->num_blocks : 0;
+  return k;
 }
 
 dsa_status check_ptr(const void *ptr, bool needed, const char *name) {
@@ -136,9 +167,11 @@ int64_t forward_ld(const dsa_problem *p) {
 }
 
 dsa::AttnArgs attn_args(const dsa_problem *p, const uint16_t *q, const uint16_t *kv,
-                        const int32_t *idx, uint16_t *out, float *lse, void *ws, size_t wsb) {
+                        const int32_t *idx, uint16_t *out, float *lse, void *ws, size_t wsb,
+                        const dsa_paged_kv *pg = nullptr) {
   dsa::AttnArgs a;
   a.seq = layout_of(p);
+  a.pg = paged_of(pg);
   a.q = q;
   a.kv = kv;
   a.idx = idx;
@@ -172,9 +205,10 @@ dsa::TopkArgs topk_args(const dsa_problem *p, const float *scores, int64_t ld, i
 
 dsa::IndexerArgs indexer_args(const dsa_problem *p, const uint8_t *q_fp8, const float *q_scale,
                               const float *w, const uint8_t *k_fp8, const float *k_scale,
-                              float *scores, int64_t ld) {
+                              float *scores, int64_t ld, const dsa_paged_kv *pg = nullptr) {
   dsa::IndexerArgs a;
   a.seq = layout_of(p);
+  a.pg = paged_of(pg);
   a.q_fp8 = q_fp8;
   a.q_scale = q_scale;
   a.w = w;
@@ -249,18 +283,41 @@ size_t dsa_workspace_bytes(const dsa_problem *p, int which) {
   }
 }
 
-dsa_status dsa_indexer_scores(const dsa_problem *p, const uint8_t *q_fp8, const float *q_scale,
-                              const float *w, const uint8_t *k_fp8, const float *k_scale,
-                              float *scores, int64_t ld_scores, void *stream) {
+}  // extern "C"
+
+namespace {
+
+dsa_status indexer_impl(const dsa_problem *p, const dsa_paged_kv *pg, const uint8_t *q_fp8,
+                        const float *q_scale, const float *w, const uint8_t *k_fp8,
+                        const float *k_scale, float *scores, int64_t ld_scores, void *stream) {
   DSA_TRY(check_problem(p));
+  if (pg != nullptr) DSA_TRY(check_paged(p, pg));
   DSA_TRY(check_indexer_dims(p));
   DSA_TRY(check_ld(p, ld_scores));
   DSA_TRY(check_indexer_ptrs(p, q_fp8, q_scale, w, k_fp8, k_scale));
   DSA_TRY(check_ptr(scores, p->total_q > 0, "scores"));
   return hip_status(dsa::launch_indexer(indexer_args(p, q_fp8, q_scale, w, k_fp8, k_scale,
-                                                     scores, ld_scores),
+                                                     scores, ld_scores, pg),
                                         static_cast<hipStream_t>(stream)),
                     "indexer launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_indexer_scores(const dsa_problem *p, const uint8_t *q_fp8, const float *q_scale,
+                              const float *w, const uint8_t *k_fp8, const float *k_scale,
+                              float *scores, int64_t ld_scores, void *stream) {
+  return indexer_impl(p, nullptr, q_fp8, q_scale, w, k_fp8, k_scale, scores, ld_scores, stream);
+}
+
+dsa_status dsa_indexer_scores_paged(const dsa_problem *p, const dsa_paged_kv *pg,
+                                    const uint8_t *q_fp8, const float *q_scale, const float *w,
+                                    const uint8_t *k_cache, const float *ks_cache, float *scores,
+                                    int64_t ld_scores, void *stream) {
+  if (pg == nullptr) return fail(DSA_ERR_INVALID_ARGUMENT, "paged-cache description is NULL");
+  return indexer_impl(p, pg, q_fp8, q_scale, w, k_cache, ks_cache, scores, ld_scores, stream);
 }
 
 dsa_status dsa_topk(const dsa_problem *p, const float *scores, int64_t ld_scores,
@@ -280,30 +337,36 @@ dsa_status dsa_topk(const dsa_problem *p, const float *scores, int64_t ld_scores
                     "top-k launch");
 }
 
-dsa_status dsa_sparse_attn(const dsa_problem *p, const uint16_t *q, const uint16_t *kv,
-                           const int32_t *topk_idx, uint16_t *out, float *lse, void *workspace,
-                           size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+dsa_status attn_impl(const dsa_problem *p, const dsa_paged_kv *pg, const uint16_t *q,
+                     const uint16_t *kv, const int32_t *topk_idx, uint16_t *out, float *lse,
+                     void *workspace, size_t workspace_bytes, void *stream) {
   DSA_TRY(check_problem(p));
-  DSA_TRY(check_attn_dims(p));
+  if (pg != nullptr) DSA_TRY(check_paged(p, pg));
+  DSA_TRY(check_attn_dims(p, pg != nullptr));
   DSA_TRY(check_attn_ptrs(p, q, kv, out, lse));
   DSA_TRY(check_ptr(topk_idx, p->total_q > 0, "topk_idx"));
   const size_t need = ws_attn(p);
   DSA_CHECK(workspace_bytes >= need && (need == 0 || workspace != nullptr), DSA_ERR_WORKSPACE,
             "attention workspace needs %zu bytes (got %zu)", need, workspace_bytes);
   return hip_status(dsa::launch_sparse_attn(attn_args(p, q, kv, topk_idx, out, lse, workspace,
-                                                      workspace_bytes),
+                                                      workspace_bytes, pg),
                                             static_cast<hipStream_t>(stream)),
                     "attention launch");
 }
 
-dsa_status dsa_forward(const dsa_problem *p, const uint8_t *q_fp8, const float *q_scale,
-                       const float *w, const uint8_t *k_fp8, const float *k_scale,
-                       const uint16_t *q, const uint16_t *kv, uint16_t *out, float *lse,
-                       int32_t *topk_idx_out, void *workspace, size_t workspace_bytes,
-                       void *stream) {
+dsa_status forward_impl(const dsa_problem *p, const dsa_paged_kv *pg, const uint8_t *q_fp8,
+                        const float *q_scale, const float *w, const uint8_t *k_fp8,
+                        const float *k_scale, const uint16_t *q, const uint16_t *kv, uint16_t *out,
+                        float *lse, int32_t *topk_idx_out, void *workspace, size_t workspace_bytes,
+                        void *stream) {
   DSA_TRY(check_problem(p));
+  if (pg != nullptr) DSA_TRY(check_paged(p, pg));
   DSA_TRY(check_indexer_dims(p));
-  DSA_TRY(check_attn_dims(p));
+  DSA_TRY(check_attn_dims(p, pg != nullptr));
   DSA_TRY(check_indexer_ptrs(p, q_fp8, q_scale, w, k_fp8, k_scale));
   DSA_TRY(check_attn_ptrs(p, q, kv, out, lse));
   if (topk_idx_out != nullptr) DSA_TRY(check_ptr(topk_idx_out, p->total_q > 0, "topk_idx_out"));
@@ -320,13 +383,49 @@ dsa_status dsa_forward(const dsa_problem *p, const uint8_t *q_fp8, const float *
   void *attn_ws = base + ws.scores + ws.idx + ws.topk;
   const int64_t ld = forward_ld(p);
   DSA_TRY(hip_status(dsa::launch_indexer(indexer_args(p, q_fp8, q_scale, w, k_fp8, k_scale,
-                                                      scores, ld), st),
+                                                      scores, ld, pg), st),
                      "indexer launch"));
   DSA_TRY(hip_status(dsa::launch_topk(topk_args(p, scores, ld, idx, topk_ws, ws.topk), st),
                      "top-k launch"));
-  return hip_status(dsa::launch_sparse_attn(attn_args(p, q, kv, idx, out, lse, attn_ws, ws.attn),
+  return hip_status(dsa::launch_sparse_attn(attn_args(p, q, kv, idx, out, lse, attn_ws, ws.attn, pg),
                                             st),
                     "attention launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_sparse_attn(const dsa_problem *p, const uint16_t *q, const uint16_t *kv,
+                           const int32_t *topk_idx, uint16_t *out, float *lse, void *workspace,
+                           size_t workspace_bytes, void *stream) {
+  return attn_impl(p, nullptr, q, kv, topk_idx, out, lse, workspace, workspace_bytes, stream);
+}
+
+dsa_status dsa_sparse_attn_paged(const dsa_problem *p, const dsa_paged_kv *pg, const uint16_t *q,
+                                 const uint16_t *kv_cache, const int32_t *topk_idx, uint16_t *out,
+                                 float *lse, void *workspace, size_t workspace_bytes, void *stream) {
+  if (pg == nullptr) return fail(DSA_ERR_INVALID_ARGUMENT, "paged-cache description is NULL");
+  return attn_impl(p, pg, q, kv_cache, topk_idx, out, lse, workspace, workspace_bytes, stream);
+}
+
+dsa_status dsa_forward(const dsa_problem *p, const uint8_t *q_fp8, const float *q_scale,
+                       const float *w, const uint8_t *k_fp8, const float *k_scale,
+                       const uint16_t *q, const uint16_t *kv, uint16_t *out, float *lse,
+                       int32_t *topk_idx_out, void *workspace, size_t workspace_bytes,
+                       void *stream) {
+  return forward_impl(p, nullptr, q_fp8, q_scale, w, k_fp8, k_scale, q, kv, out, lse, topk_idx_out,
+                      workspace, workspace_bytes, stream);
+}
+
+dsa_status dsa_forward_paged(const dsa_problem *p, const dsa_paged_kv *pg, const uint8_t *q_fp8,
+                             const float *q_scale, const float *w, const uint8_t *k_cache,
+                             const float *ks_cache, const uint16_t *q, const uint16_t *kv_cache,
+                             uint16_t *out, float *lse, int32_t *topk_idx_out, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  if (pg == nullptr) return fail(DSA_ERR_INVALID_ARGUMENT, "paged-cache description is NULL");
+  return forward_impl(p, pg, q_fp8, q_scale, w, k_cache, ks_cache, q, kv_cache, out, lse,
+                      topk_idx_out, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -164,8 +164,10 @@ __device__ __forceinline__ float reduce_four_blocks(float p0, float p1, float p2
 
 // Prefill: grid (key split, query tile, sequence).  Each wave keeps QW query
 // rows resident (A operands + weights); the workgroup streams its key range
-// through double-buffered LDS tiles shared by all waves.
-template <int HB, int QW>
+// through double-buffered LDS tiles shared by all waves.  With kPaged the
+// keys come from block-table caches; a 64-key tile never crosses a block
+// (tiles start at multiples of 64, blocks hold a multiple of 64 rows).
+template <int HB, int QW, bool kPaged>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
 void indexer_prefill_kernel(IndexerArgs p, int key_split) {
   constexpr int QT = kWaves * QW;
@@ -173,7 +175,8 @@ void indexer_prefill_kernel(IndexerArgs p, int key_split) {
   __shared__ __attribute__((aligned(16))) uint8_t linq[kWaves][QW * kLinPieces * 128];
   __shared__ float lininv[kWaves][QW];
 
-  const SeqInfo s = load_seq(p.seq, (int)__builtin_amdgcn_workgroup_id_z());
+  const int sb = (int)__builtin_amdgcn_workgroup_id_z();
+  const SeqInfo s = load_seq(p.seq, sb);
   const int64_t qlen = s.q1 - s.q0;
   const int64_t row_begin = (int64_t)__builtin_amdgcn_workgroup_id_y() * QT;
   if (row_begin >= qlen || s.kvlen <= 0) return;
@@ -221,13 +224,17 @@ void indexer_prefill_kernel(IndexerArgs p, int key_split) {
   v4i stage[2];
   const uint8_t *kbase = p.k_fp8 + s.kv0 * d;
   auto fetch = [&](int t0) {
+    // paged: the tile's first row (a tile stays inside one block; a tile
+    // past the keys reads tile 0, whose values are then zeroed)
+    const int64_t rb = kPaged ? kv_row<true>(p.pg, s, sb, t0 < kvlen ? t0 : 0) : 0;
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int chunk = tid + 256 * e, n = chunk >> 3, j = chunk & 7;
       const int key = t0 + n;
       const bool ok = key < kvlen && 16 * j < d;
-      const v4i x = *reinterpret_cast<const v4i *>(
-          kbase + (int64_t)(key < kvlen ? key : 0) * d + (16 * j < d ? 16 * j : 0));
+      const uint8_t *src = kPaged ? p.k_fp8 + (rb + n) * d
+                                  : kbase + (int64_t)(key < kvlen ? key : 0) * d;
+      const v4i x = *reinterpret_cast<const v4i *>(src + (16 * j < d ? 16 * j : 0));
       stage[e] = ok ? x : v4i{0, 0, 0, 0};
     }
   };
@@ -273,7 +280,8 @@ void indexer_prefill_kernel(IndexerArgs p, int key_split) {
     const bool has_next = t0 + kKeyTile < key_end;
     fetch(t0 + kKeyTile);
     const int my_key = t0 + lane;
-    const float ks = kscale[my_key < kvlen ? my_key : 0];
+    const float ks = kPaged ? p.k_scale[kv_row<true>(p.pg, s, sb, t0) + lane]   // t0 < kvlen
+                            : kscale[my_key < kvlen ? my_key : 0];
 
     float part[QW][4];
 #pragma unroll
@@ -308,7 +316,7 @@ void indexer_prefill_kernel(IndexerArgs p, int key_split) {
 // straight from HBM into MFMA B operands; nothing goes through LDS.
 constexpr int kDecodeChunk = 1024;  // keys per workgroup (4 waves x 256)
 
-template <int HB>
+template <int HB, bool kPaged>
 __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs p) {
   const int64_t row = __builtin_amdgcn_workgroup_id_y();
   SeqInfo s;
@@ -342,10 +350,27 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs p) {
                        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32)) << 32);
     return __builtin_amdgcn_make_buffer_rsrc((void *)(uintptr_t)u, (short)0, bytes, 0x00020000);
   };
-  const __amdgpu_buffer_rsrc_t krs = rsrc(p.k_fp8 + (s.kv0 + wave_begin) * d, nk * d);
-  const __amdgpu_buffer_rsrc_t srs = rsrc(p.k_scale + s.kv0 + wave_begin, nk * 4);
+  const __amdgpu_buffer_rsrc_t krs = rsrc(p.k_fp8 + (kPaged ? 0 : (s.kv0 + wave_begin) * d), kPaged ? 0 : nk * d);
+  const __amdgpu_buffer_rsrc_t srs = rsrc(p.k_scale + (kPaged ? 0 : s.kv0 + wave_begin), kPaged ? 0 : nk * 4);
   const int koff = 32 * g < d ? c * d + 32 * g : 0x40000000;
   auto load_step = [&](int st, v8i (&kr)[4], float &ks) {
+    if (kPaged) {
+      // one block per 64-key step: descriptors over that step's rows
+      const int cnt = nk - 64 * st < 0 ? 0 : (nk - 64 * st > 64 ? 64 : nk - 64 * st);
+      const int64_t at = wave_begin + 64 * st;
+      const int64_t rb = kv_row<true>(p.pg, s, b, at < s.kvlen ? at : 0);
+      const __amdgpu_buffer_rsrc_t kst = rsrc(p.k_fp8 + rb * d, cnt * d);
+      const __amdgpu_buffer_rsrc_t sst = rsrc(p.k_scale + rb, cnt * 4);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int so = kb * 16 * d;
+        const v4i lo = __builtin_amdgcn_raw_buffer_load_b128(kst, koff, so, 0);
+        const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(kst, koff + 16, so, 0);
+        kr[kb] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      }
+      ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sst, lane * 4, 0, 0));
+      return;
+    }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       const int so = (st * 64 + kb * 16) * d;
@@ -409,14 +434,20 @@ hipError_t launch_prefill(const IndexerArgs &a, hipStream_t stream) {
   const int64_t split = split_of(m);
   const int64_t nsplit = 8 * m;
   dim3 grid((unsigned)nsplit, (unsigned)qtiles, (unsigned)a.seq.batch);
-  hipLaunchKernelGGL((indexer_prefill_kernel<HB, QW>), grid, dim3(256), 0, stream, a, (int)split);
+  if (a.pg.table != nullptr)
+    hipLaunchKernelGGL((indexer_prefill_kernel<HB, QW, true>), grid, dim3(256), 0, stream, a, (int)split);
+  else
+    hipLaunchKernelGGL((indexer_prefill_kernel<HB, QW, false>), grid, dim3(256), 0, stream, a, (int)split);
   return hipGetLastError();
 }
 
 template <int HB>
 hipError_t launch_decode(const IndexerArgs &a, hipStream_t stream) {
   dim3 grid((unsigned)((a.seq.max_kv_len + kDecodeChunk - 1) / kDecodeChunk), (unsigned)a.seq.total_q);
-  hipLaunchKernelGGL((indexer_decode_kernel<HB>), grid, dim3(256), 0, stream, a);
+  if (a.pg.table != nullptr)
+    hipLaunchKernelGGL((indexer_decode_kernel<HB, true>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((indexer_decode_kernel<HB, false>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -17,8 +17,18 @@ struct SeqLayout {
   int64_t total_q, total_kv, max_q_len, max_kv_len;
 };
 
+// Paged key / KV caches: key position s of sequence b is row
+// table[b * max_blocks + s / block_size] * block_size + s % block_size.
+struct PagedKV {
+  const int32_t *table;   // nullptr: rows are packed, kv_offsets[b] + s
+  int32_t block_shift;    // log2(block_size), block_size a power of two >= 64
+  int32_t max_blocks;     // row stride of the table
+  int32_t num_blocks;     // num_blocks << block_shift < 2^31
+};
+
 struct IndexerArgs {
   SeqLayout seq;
+  PagedKV pg;
   const uint8_t *q_fp8;
   const float *q_scale;
   const float *w;
@@ -42,6 +52,7 @@ struct TopkArgs {
 
 struct AttnArgs {
   SeqLayout seq;
+  PagedKV pg;
   const uint16_t *q;
   const uint16_t *kv;
   const int32_t *idx;
@@ -114,6 +125,22 @@ __device__ __forceinline__ int find_seq(const SeqLayout &L, int64_t r) {
     cnt += __popcll(__ballot(le));
   }
   return cnt > 0 ? cnt - 1 : 0;
+}
+
+// Cache row of key position pos (0 <= pos < s.kvlen) of sequence b.  With a
+// block table, the block index and the table entry are clamped in bounds.
+template <bool kPaged>
+__device__ __forceinline__ int64_t kv_row(const PagedKV &pg, const SeqInfo &s, int b, int64_t pos) {
+  if (!kPaged) return s.kv0 + pos;
+  const int p32 = (int)pos;   // positions fit int32 (validated on the host)
+  int blk = p32 >> pg.block_shift;
+  blk = blk < 0 ? 0 : (blk >= pg.max_blocks ? pg.max_blocks - 1 : blk);
+  int phys = pg.table[b * pg.max_blocks + blk];
+  phys = phys < 0 ? 0 : (phys >= pg.num_blocks ? pg.num_blocks - 1 : phys);
+  int slot = p32 - (blk << pg.block_shift);
+  const int bmask = (1 << pg.block_shift) - 1;
+  slot = slot < 0 ? 0 : (slot > bmask ? bmask : slot);
+  return (int64_t)((phys << pg.block_shift) + slot);
 }
 
 // Sequence of packed query row r and its metadata.  Decode batches hold one

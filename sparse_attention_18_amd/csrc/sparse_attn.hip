@@ -42,6 +42,8 @@
 // softmax denominator per head to the workspace; a small combine kernel then
 // rescales the ranges to their common maximum frame (the usual merge of
 // partial softmax sums) and writes out and lse.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -105,6 +107,39 @@ __device__ __forceinline__ void lds_dma16_x4(uint32_t voff, uint64_t b0, uint64_
       : "memory");
 }
 
+// Vector-address form (paged caches, whose rows may lie more than 4 GB
+// apart): lane i's 16 bytes come from a_k(i) + 1024 k and land at
+// M0 + 1024 k + 16 i, so a_k is passed already shifted by -1024 k.
+__device__ __forceinline__ void lds_dma16v_x4(uint64_t a0, uint64_t a1, uint64_t a2, uint64_t a3,
+                                              uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %5\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "global_load_lds_dwordx4 %2, off offset:1024\n\t"
+      "global_load_lds_dwordx4 %3, off offset:2048\n\t"
+      "global_load_lds_dwordx4 %4, off offset:3072\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3), "s"(lds_base)
+      : "memory");
+}
+
+__device__ __forceinline__ void lds_dma16v_x1(uint64_t a0, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(a0), "s"(lds_base)
+      : "memory");
+}
+
 __device__ __forceinline__ void lds_dma16_x1(uint32_t voff, uint64_t b0, uint32_t lds_base) {
   uint32_t saved;
   asm volatile(
@@ -139,7 +174,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-template <int NW>
+template <int NW, bool kPaged>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_sparse_attn_kernel(AttnArgs p) {
   constexpr int H = NW * 32;
@@ -203,6 +238,12 @@ void mla_sparse_attn_kernel(AttnArgs p) {
       vals[e] = (v >= 0 && v < s.kvlen) ? v : -1;
       cnt += vals[e] >= 0;
     }
+    if (kPaged) {
+      // positions become cache rows here, once per token (rows < 2^31)
+#pragma unroll
+      for (int e = 0; e < per; ++e)
+        if (vals[e] >= 0) vals[e] = (int)kv_row<true>(p.pg, s, b, vals[e]);
+    }
     const int inc = (int)wave_scan<0>((uint32_t)cnt);
     if (lane == 63) s_scan[wave] = inc;
     if (tid == 0) s_flag = 0;
@@ -238,27 +279,41 @@ void mla_sparse_attn_kernel(AttnArgs p) {
   constexpr int kRB = 4 / NW;
   constexpr int kWindows = 3 * kRB;
   // Uniform sequence base; a row's byte offset fits in 32 bits (the host
-  // bounds max_kv_len * 1152 below 2^32 for this path).
-  const uint8_t *kvseq = reinterpret_cast<const uint8_t *>(p.kv + s.kv0 * (int64_t)kD);
-  auto gather_setup = [&](int tl, uint32_t (&voff)[kRB]) {
+  // bounds max_kv_len * 1152 below 2^32 for this path).  Paged caches: each
+  // lane's row address is a full 64-bit value (GOff).
+  using GOff = typename std::conditional<kPaged, uint64_t, uint32_t>::type;
+  const uint8_t *kvseq = reinterpret_cast<const uint8_t *>(p.kv + (kPaged ? 0 : s.kv0 * (int64_t)kD));
+  auto gather_setup = [&](int tl, GOff (&voff)[kRB]) {
 #pragma unroll
     for (int q = 0; q < kRB; ++q) {
       const int row = 8 * (wave + NW * q) + (lane >> 3);
       const int r = tl * kBN + row;
       const int gi = idxr[r < nrows ? r : 0];
-      voff[q] = (uint32_t)gi * (uint32_t)(kD * 2) + 16 * ((lane & 7) ^ ((row >> 1) & 7));
+      const uint32_t in_row = 16 * ((lane & 7) ^ ((row >> 1) & 7));
+      if constexpr (kPaged)
+        voff[q] = (uint64_t)(uintptr_t)kvseq + (uint64_t)(uint32_t)gi * (uint64_t)(kD * 2) + in_row;
+      else
+        voff[q] = (uint32_t)gi * (uint32_t)(kD * 2) + in_row;
     }
     return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(DSA_LDS uint8_t *)kvbuf[tl % kStages]);
   };
   // Window w: row block wave + NW*(w/3), chunk groups 4*(w%3) .. (+3, or 8).
-  auto gather_window = [&](const uint32_t (&voff)[kRB], uint32_t base, int w) {
+  auto gather_window = [&](const GOff (&voff)[kRB], uint32_t base, int w) {
     const int q = w / 3, win = w % 3;
     const uint32_t lb = __builtin_amdgcn_readfirstlane(base + ((wave + NW * q) * kGroups + 4 * win) * kBlock);
-    const uint8_t *g = kvseq + 128 * 4 * win;      // chunk group 4*win
-    if (win < 2)
-      lds_dma16_x4(voff[q], sbase(g), sbase(g + 128 - 1024), sbase(g + 256 - 2048), sbase(g + 384 - 3072), lb);
-    else
-      lds_dma16_x1(voff[q], sbase(g), lb);
+    if constexpr (kPaged) {
+      const uint64_t a = voff[q] + 128 * 4 * win;   // chunk group 4*win
+      if (win < 2)
+        lds_dma16v_x4(a, a + 128 - 1024, a + 256 - 2048, a + 384 - 3072, lb);
+      else
+        lds_dma16v_x1(a, lb);
+    } else {
+      const uint8_t *g = kvseq + 128 * 4 * win;      // chunk group 4*win
+      if (win < 2)
+        lds_dma16_x4(voff[q], sbase(g), sbase(g + 128 - 1024), sbase(g + 256 - 2048), sbase(g + 384 - 3072), lb);
+      else
+        lds_dma16_x1(voff[q], sbase(g), lb);
+    }
   };
 
   const float sl2 = p.scale * kLog2e;
@@ -310,7 +365,7 @@ void mla_sparse_attn_kernel(AttnArgs p) {
       constexpr int KS = kD / 16, LA = 3, NPV = 2 * MB * NW;
       static_assert(NPV <= KS, "P.V MFMAs ride along the S^T chain");
       const DSA_LDS uint8_t *tbq = (const DSA_LDS uint8_t *)kvbuf[tq % kStages];
-      uint32_t src[kRB];
+      GOff src[kRB];
       uint32_t gbase = 0;
       if (gnext) gbase = gather_setup(tq + 1, src);
       v16f sc;
@@ -401,7 +456,7 @@ void mla_sparse_attn_kernel(AttnArgs p) {
     }
     if (ntiles > 0) {
       {
-        uint32_t src[kRB];
+        GOff src[kRB];
         const uint32_t gbase = gather_setup(0, src);
 #pragma unroll
         for (int w = 0; w < kWindows; ++w) gather_window(src, gbase, w);
@@ -533,6 +588,7 @@ constexpr int kSmallThreads = 256;
 constexpr int kSmallMaxD = 1024;
 constexpr int kSmallMaxK = 4096;
 
+template <bool kPaged>
 __global__ __launch_bounds__(kSmallThreads) void small_sparse_attn_kernel(AttnArgs p) {
   __shared__ float qs[kSmallMaxD];
   __shared__ float prob[kSmallMaxK];
@@ -546,7 +602,8 @@ __global__ __launch_bounds__(kSmallThreads) void small_sparse_attn_kernel(AttnAr
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int i = tid; i < k; i += kSmallThreads) {
     const int v = p.idx[t * k + i];
-    rows[i] = (v >= 0 && v < s.kvlen) ? v : -1;
+    // cache row (packed: relative to the sequence's first row)
+    rows[i] = (v >= 0 && v < s.kvlen) ? (kPaged ? (int)kv_row<true>(p.pg, s, b, v) : v) : -1;
   }
   auto block_reduce = [&](float v, bool is_max) {
     for (int d = 32; d >= 1; d >>= 1) {
@@ -568,7 +625,7 @@ __global__ __launch_bounds__(kSmallThreads) void small_sparse_attn_kernel(AttnAr
     for (int i = tid; i < k; i += kSmallThreads) {
       float x = -INFINITY;
       if (rows[i] >= 0) {
-        const uint16_t *kr = p.kv + (s.kv0 + rows[i]) * (int64_t)D;
+        const uint16_t *kr = p.kv + ((kPaged ? 0 : s.kv0) + rows[i]) * (int64_t)D;
         float acc = 0.f;
         for (int d = 0; d < D; ++d) acc = fmaf(qs[d], bf16_bits_to_f32(kr[d]), acc);
         x = acc * p.scale;
@@ -589,7 +646,7 @@ __global__ __launch_bounds__(kSmallThreads) void small_sparse_attn_kernel(AttnAr
     for (int d = tid; d < DL; d += kSmallThreads) {
       float acc = 0.f;
       for (int i = 0; i < k; ++i)
-        if (rows[i] >= 0) acc = fmaf(prob[i], bf16_bits_to_f32(p.kv[(s.kv0 + rows[i]) * (int64_t)D + d]), acc);
+        if (rows[i] >= 0) acc = fmaf(prob[i], bf16_bits_to_f32(p.kv[((kPaged ? 0 : s.kv0) + rows[i]) * (int64_t)D + d]), acc);
       p.out[(t * H + h) * DL + d] = (uint16_t)f32_to_bf16_bits(acc * inv);
     }
   }
@@ -624,17 +681,28 @@ hipError_t launch_sparse_attn(const AttnArgs &args, hipStream_t stream) {
   if (a.nsplit > 1 && (a.workspace == nullptr || a.workspace_bytes < sparse_attn_workspace_bytes(a)))
     return hipErrorInvalidValue;   // the ABI layer checks the size first
   const dim3 grid((unsigned)(a.seq.total_q * a.nsplit));
+  const bool paged = a.pg.table != nullptr;
   if (mfma_shape(a)) {
     switch (a.heads / 32) {
-      case 1: hipLaunchKernelGGL(mla_sparse_attn_kernel<1>, grid, dim3(64), 0, stream, a); break;
-      case 2: hipLaunchKernelGGL(mla_sparse_attn_kernel<2>, grid, dim3(128), 0, stream, a); break;
-      default: hipLaunchKernelGGL(mla_sparse_attn_kernel<4>, grid, dim3(256), 0, stream, a); break;
+      case 1:
+        if (paged) hipLaunchKernelGGL((mla_sparse_attn_kernel<1, true>), grid, dim3(64), 0, stream, a);
+        else hipLaunchKernelGGL((mla_sparse_attn_kernel<1, false>), grid, dim3(64), 0, stream, a);
+        break;
+      case 2:
+        if (paged) hipLaunchKernelGGL((mla_sparse_attn_kernel<2, true>), grid, dim3(128), 0, stream, a);
+        else hipLaunchKernelGGL((mla_sparse_attn_kernel<2, false>), grid, dim3(128), 0, stream, a);
+        break;
+      default:
+        if (paged) hipLaunchKernelGGL((mla_sparse_attn_kernel<4, true>), grid, dim3(256), 0, stream, a);
+        else hipLaunchKernelGGL((mla_sparse_attn_kernel<4, false>), grid, dim3(256), 0, stream, a);
+        break;
     }
     if (a.nsplit > 1)
       hipLaunchKernelGGL(combine_splits_kernel, dim3((unsigned)(a.seq.total_q * a.heads)), dim3(128), 0,
                          stream, a, (int)a.heads);
   } else {
-    hipLaunchKernelGGL(small_sparse_attn_kernel, grid, dim3(kSmallThreads), 0, stream, a);
+    if (paged) hipLaunchKernelGGL(small_sparse_attn_kernel<true>, grid, dim3(kSmallThreads), 0, stream, a);
+    else hipLaunchKernelGGL(small_sparse_attn_kernel<false>, grid, dim3(kSmallThreads), 0, stream, a);
   }
   return hipGetLastError();
 }

@@ -194,3 +194,47 @@ def chunk_views(inputs: dict, chunk: int):
     L = inputs["q_offsets"][1]
     for r0 in range(0, L, chunk):
         yield r0, slice(r0, min(L, r0 + chunk))
+
+
+def paged_caches(inp: dict, block_size: int, seed: int = 0, extra_blocks: int = 5,
+                 high_base_rows: int = 0, device="cuda"):
+    """Block-table copies of a workload's packed key and latent KV caches
+    (the serving layout of dsa_paged_kv): every sequence's rows are cut into
+    blocks of ``block_size`` and scattered over shuffled physical blocks,
+    with ``extra_blocks`` unused ones among them.  With ``high_base_rows`` the
+    used blocks start that many rows into the caches (the rows below stay
+    zero), e.g. to place them past 4 GB.  Unused table entries are -1.
+    Returns (block_table [B, max_blocks] int32 on the CPU, num_blocks,
+    k_cache [nb, bs, d_I] u8, ks_cache [nb, bs] f32, kv_cache [nb, bs, D] bf16)."""
+    kv_off = [int(x) for x in inp["kv_offsets"]]
+    B = len(kv_off) - 1
+    lens = [kv_off[b + 1] - kv_off[b] for b in range(B)]
+    nblk = [(n + block_size - 1) // block_size for n in lens]
+    max_blocks = max(1, max(nblk))
+    used = sum(nblk)
+    g = torch.Generator().manual_seed(seed)
+    base_blk = (high_base_rows + block_size - 1) // block_size
+    phys = (torch.randperm(used + extra_blocks, generator=g)[:used] + base_blk).tolist()
+    num_blocks = base_blk + used + extra_blocks
+    table = torch.full((B, max_blocks), -1, dtype=torch.int32)
+    src, dst = [], []
+    it = iter(phys)
+    for b in range(B):
+        for j in range(nblk[b]):
+            pb = next(it)
+            table[b, j] = pb
+            n = min(block_size, lens[b] - j * block_size)
+            src.append(torch.arange(kv_off[b] + j * block_size, kv_off[b] + j * block_size + n))
+            dst.append(torch.arange(pb * block_size, pb * block_size + n))
+    src = torch.cat(src).to(device) if src else torch.zeros(0, dtype=torch.long, device=device)
+    dst = torch.cat(dst).to(device) if dst else torch.zeros(0, dtype=torch.long, device=device)
+    nrows = num_blocks * block_size
+    k, ks, kv = inp["k_fp8"].to(device), inp["k_scale"].to(device), inp["kv"].to(device)
+    k_cache = torch.zeros(nrows, k.shape[1], dtype=k.dtype, device=device)
+    ks_cache = torch.zeros(nrows, dtype=ks.dtype, device=device)
+    kv_cache = torch.zeros(nrows, kv.shape[1], dtype=kv.dtype, device=device)
+    k_cache[dst] = k[src]
+    ks_cache[dst] = ks[src]
+    kv_cache[dst] = kv[src]
+    return (table, num_blocks, k_cache.view(num_blocks, block_size, -1),
+            ks_cache.view(num_blocks, block_size), kv_cache.view(num_blocks, block_size, -1))
