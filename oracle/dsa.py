@@ -25,6 +25,12 @@ What it computes, stage by stage, in the order the pages give:
    gather, softmax-weighted sum): MQA/MLA over the selected rows only.  All
    heads of a token share one latent KV row per key; the key is the whole
    row (latent + rope), the value its latent part.
+4. Indexer alignment loss (training).  ivugangingo.com article, section
+   "DeepSeek sparse attention pre-training continues": the indexer is trained
+   with a KL loss towards the attention's distribution, over all causal keys
+   in the dense warm-up and over the selected keys afterwards.  The loss of a
+   token is KL(head-summed, L1-normalised attention probabilities || softmax
+   of the indexer scores), with its gradient taken with respect to the scores.
 
 Readings where the pages are silent or garbled (each listed in the design doc):
 the indexer formula and FP8 format; causality (a key is visible iff its
@@ -160,3 +166,85 @@ def forward_rows(q, w, k, pos, q_attn, kv, topk: int, scale: float, d_latent: in
     outs, lses = zip(*(sparse_attention_row(q_attn[r], kv, idx[r], scale, d_latent)
                        for r in range(len(pos))))
     return scores, idx, np.stack(outs), np.stack(lses)
+
+
+# ---------------------------------------------------------------------------
+# Stage 4 (training): indexer alignment loss
+# ---------------------------------------------------------------------------
+# ivugangingo.com article on DeepSeek-V3.2, section "DeepSeek sparse attention
+# pre-training continues": during the dense warm-up only the indexer learns,
+# through a Kullback-Leibler loss that pulls its distribution towards the
+# dense attention's; in the sparse stage (k = 2048 selected keys per query)
+# the indexer's gradients come only from that alignment loss, taken over the
+# selected keys.  The pages give no formula; the readings used here:
+#   * the attention "distribution" of a token is its per-head softmax
+#     probabilities summed over the heads and L1-normalised over the keys;
+#   * the indexer's distribution is the softmax of its scores over the same
+#     keys (all causal keys in the warm-up, the selected set afterwards);
+#   * the loss of a token is KL(attention || indexer), with the attention side
+#     held fixed: its gradient is taken with respect to the indexer scores only.
+def attention_target_row(q_row, kv, keys, scale: float) -> np.ndarray:
+    """Head-summed, L1-normalised attention distribution of one token over `keys`.
+
+    q_row [H, D] and kv [S, D] float64; keys [m] row indices into kv (m >= 1).
+    For each head, p_h = softmax(scale * q_h . kv[keys]); the target is
+    sum_h p_h divided by its total (which is H).
+    """
+    rows = kv[np.asarray(keys)]
+    logits = scale * (q_row @ rows.T)                    # [H, m]
+    e = np.exp(logits - logits.max(axis=1, keepdims=True))
+    per_head = e / e.sum(axis=1, keepdims=True)          # each row sums to 1
+    summed = per_head.sum(axis=0)
+    return summed / summed.sum()
+
+
+def indexer_kl_row(scores_sel, target):
+    """KL(target || softmax(scores_sel)) and its gradient with respect to scores_sel.
+
+    With q = softmax(scores_sel): loss = sum_i target_i * (log target_i - log q_i),
+    terms with target_i = 0 being 0.  Since sum_i target_i = 1, the derivative
+    of the loss with respect to scores_sel[i] is q_i - target_i.
+    """
+    s = np.asarray(scores_sel, dtype=np.float64)
+    p = np.asarray(target, dtype=np.float64)
+    mx = s.max()
+    log_q = s - (mx + np.log(np.exp(s - mx).sum()))
+    pos = p > 0
+    loss = float(np.sum(p[pos] * (np.log(p[pos]) - log_q[pos])))
+    return loss, np.exp(log_q) - p
+
+
+def alignment_loss_rows(q_attn, kv, scores, pos, scale: float, idx=None):
+    """Alignment loss of a set of query rows of one sequence, in float64.
+
+    q_attn [R, H, D], kv [S, D]; scores: R score rows, row r holding at least
+    pos[r] + 1 entries (the indexer's scores of that query, key position as
+    index).  Dense warm-up form (idx None): row r's keys are 0..pos[r].
+    Sparse form: idx [R, k] selected positions, -1 entries skipped (the others
+    taken as given, as the attention takes them).
+    Returns (loss [R], grads): grads[r] is the gradient over the row's keys --
+    dense: an array of length pos[r] + 1; sparse: [k], aligned with idx[r],
+    zero at the -1 entries.  A row with no key has loss 0.
+    """
+    losses, grads = [], []
+    for r in range(len(pos)):
+        row_scores = np.asarray(scores[r], dtype=np.float64)
+        if idx is None:
+            keys = np.arange(int(pos[r]) + 1)
+        else:
+            sel = np.asarray(idx[r])
+            keys = sel[sel >= 0]
+        if keys.size == 0:
+            losses.append(0.0)
+            grads.append(np.zeros(0 if idx is None else len(idx[r])))
+            continue
+        target = attention_target_row(q_attn[r], kv, keys, scale)
+        loss, g = indexer_kl_row(row_scores[keys], target)
+        losses.append(loss)
+        if idx is None:
+            grads.append(g)
+        else:
+            full = np.zeros(len(idx[r]))
+            full[np.asarray(idx[r]) >= 0] = g
+            grads.append(full)
+    return np.array(losses), grads
