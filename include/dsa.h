@@ -201,6 +201,45 @@ dsa_status dsa_forward_paged(const dsa_problem *p, const dsa_paged_kv *pg, const
                              uint16_t *out, float *lse, int32_t *topk_idx_out, void *workspace,
                              size_t workspace_bytes, void *stream);
 
+/*
+ * Indexer alignment loss (training).  The ivugangingo.com article, section
+ * "DeepSeek sparse attention pre-training continues": the indexer is trained
+ * with a Kullback-Leibler loss towards the main attention's distribution,
+ * over all causal keys during the dense warm-up and over the selected keys in
+ * the sparse stage, where that loss is the indexer's only gradient source.
+ * The pages give no formula; this library computes, for query row r with key
+ * set K_r (dense: positions 0..pos(r); sparse: the valid entries of
+ * topk_idx[r], as in dsa_sparse_attn):
+ *   logit[h, s] = softmax_scale * q[r, h, :] . kv[kv_offsets[b] + s, :]   (as in stage 3)
+ *   p_s  = (1/H) sum_h exp(logit[h, s] - lse[r, h])     attention target over K_r
+ *   q_s  = exp(I_s) / sum_{s' in K_r} exp(I_s')         I_s = scores[r * ld_scores + s]
+ *   loss[r] = sum_{s in K_r} p_s (ln p_s - ln q_s)      (terms with p_s = 0 are 0)
+ *   d loss[r] / d I_s = q_s - p_s
+ * lse must be the attention's natural-log log-sum-exp over the same K_r (the
+ * lse output of dsa_sparse_attn / dsa_forward for the sparse form; of the
+ * dense causal attention for the warm-up form): each head's softmax then
+ * sums to one, and 1/H normalises the head sum.  The attention side is a
+ * fixed target; no gradient flows into q or kv.
+ *   q [total_q, H, D] bf16, kv [total_kv, D] bf16, lse [total_q, H] float
+ *   scores [total_q, ld_scores] float (read at the positions of K_r only)
+ *   topk_idx [total_q, k] int32, or NULL for the dense warm-up form
+ *   loss [total_q] float
+ *   grad: sparse, [total_q, ld_grad] with entry i of row r the derivative for
+ *         topk_idx[r, i] (0 where that entry is skipped; entries i >= k are
+ *         not written), ld_grad >= k; dense, [total_q, ld_grad] by position,
+ *         positions 0..pos(r) written, the rest untouched, ld_grad >=
+ *         max_kv_len.
+ * dsa_forward keeps its scores at the start of its workspace with
+ * ld_scores = max_kv_len rounded up to a multiple of 64, so a training step
+ * may pass that pointer (with topk_idx_out and lse from the same call).
+ * Shapes as for dsa_sparse_attn; fp32 arithmetic on bf16 products (MFMA for
+ * the (512, 64) shape).  The dense form costs O(pos) per row.
+ */
+dsa_status dsa_indexer_align_loss(const dsa_problem *p, const uint16_t *q, const uint16_t *kv,
+                                  const float *lse, const float *scores, int64_t ld_scores,
+                                  const int32_t *topk_idx, float *loss, float *grad,
+                                  int64_t ld_grad, void *stream);
+
 /* Bytes of device workspace the given entry point needs for problem p
  * (which = DSA_WS_TOPK, DSA_WS_ATTN or DSA_WS_FORWARD); 0 if none.  Returns
  * (size_t)-1 for an invalid problem (see dsa_last_error).  The paged entry

@@ -27,7 +27,7 @@ WS_TOPK, WS_ATTN, WS_FORWARD = 0, 1, 2
 
 EXPORTED = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward",
             "dsa_indexer_scores_paged", "dsa_sparse_attn_paged", "dsa_forward_paged",
-            "dsa_workspace_bytes", "dsa_last_error", "dsa_version")
+            "dsa_indexer_align_loss", "dsa_workspace_bytes", "dsa_last_error", "dsa_version")
 
 
 class DsaLibraryError(RuntimeError):
@@ -102,8 +102,10 @@ def load_library():
         lib.dsa_indexer_scores_paged.argtypes = [P, G, vp, vp, vp, vp, vp, vp, i64, vp]
         lib.dsa_sparse_attn_paged.argtypes = [P, G, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.dsa_forward_paged.argtypes = [P, G, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        lib.dsa_indexer_align_loss.argtypes = [P, vp, vp, vp, vp, i64, vp, vp, vp, i64, vp]
         for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward",
-                     "dsa_indexer_scores_paged", "dsa_sparse_attn_paged", "dsa_forward_paged"):
+                     "dsa_indexer_scores_paged", "dsa_sparse_attn_paged", "dsa_forward_paged",
+                     "dsa_indexer_align_loss"):
             getattr(lib, name).restype = ctypes.c_int
         lib.dsa_workspace_bytes.argtypes = [P, ctypes.c_int]
         lib.dsa_workspace_bytes.restype = sz
@@ -274,6 +276,30 @@ def forward(prob: Problem, q_fp8, q_scale, w, k_fp8, k_scale, q, kv, out, lse=No
         _ptr(lse, torch.float32, "lse", (c.total_q, c.heads)),
         _ptr(idx_out, torch.int32, "idx_out", (c.total_q, c.topk)),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
+
+
+def indexer_align_loss(prob: Problem, q, kv, lse, scores, loss, grad, idx=None, ld=None,
+                       stream=None):
+    """dsa_indexer_align_loss: per-row KL(attention target || indexer softmax) into
+    ``loss`` [total_q] and its gradient with respect to the scores into ``grad``.
+
+    Sparse form (``idx`` given): grad is [total_q, k], entry i for idx[:, i].
+    Dense warm-up form (``idx`` None): grad is [total_q, ld_grad] by position,
+    with ld_grad = grad.shape[1] >= max_kv_len."""
+    c = prob.c
+    D = c.d_latent + c.d_rope
+    ld = prob.ld_scores() if ld is None else int(ld)
+    if not isinstance(grad, torch.Tensor) or grad.dim() != 2:
+        raise ValueError("grad must be a 2-D tensor")
+    ld_grad = int(grad.shape[1])
+    _check(load_library().dsa_indexer_align_loss(
+        ctypes.byref(c), _ptr(q, torch.bfloat16, "q", (c.total_q, c.heads, D)),
+        _ptr(kv, torch.bfloat16, "kv", (c.total_kv, D)),
+        _ptr(lse, torch.float32, "lse", (c.total_q, c.heads)),
+        _ptr(scores, torch.float32, "scores", (c.total_q, ld)), ld,
+        _ptr(idx, torch.int32, "idx", (c.total_q, c.topk)),
+        _ptr(loss, torch.float32, "loss", (c.total_q,)),
+        _ptr(grad, torch.float32, "grad", (c.total_q, ld_grad)), ld_grad, _stream(stream)))
 
 
 class PagedKV:

@@ -429,3 +429,58 @@ dsa_status dsa_forward_paged(const dsa_problem *p, const dsa_paged_kv *pg, const
 }
 
 }  // extern "C"
+
+namespace {
+
+dsa_status align_impl(const dsa_problem *p, const uint16_t *q, const uint16_t *kv, const float *lse,
+                      const float *scores, int64_t ld_scores, const int32_t *topk_idx, float *loss,
+                      float *grad, int64_t ld_grad, void *stream) {
+  DSA_TRY(check_problem(p));
+  DSA_TRY(check_attn_dims(p));
+  DSA_TRY(check_ld(p, ld_scores));
+  const bool hq = p->total_q > 0;
+  DSA_TRY(check_ptr(q, hq, "q"));
+  DSA_TRY(check_ptr(kv, p->total_kv > 0, "kv"));
+  DSA_TRY(check_ptr(lse, hq, "lse"));
+  DSA_TRY(check_ptr(scores, hq, "scores"));
+  DSA_TRY(check_ptr(loss, hq, "loss"));
+  DSA_TRY(check_ptr(grad, hq, "grad"));
+  if (topk_idx != nullptr) DSA_TRY(check_ptr(topk_idx, hq, "topk_idx"));
+  const int64_t need = topk_idx != nullptr ? (int64_t)p->topk : p->max_kv_len;
+  DSA_CHECK(ld_grad >= need && ld_grad >= 1, DSA_ERR_INVALID_ARGUMENT,
+            "ld_grad (%lld) must be >= %s (%lld) and >= 1", (long long)ld_grad,
+            topk_idx != nullptr ? "topk" : "max_kv_len", (long long)need);
+  DSA_CHECK(p->total_q == 0 || ld_grad <= INT64_MAX / 4 / p->total_q, DSA_ERR_INVALID_ARGUMENT,
+            "grad matrix size overflows");
+  dsa::AlignArgs a;
+  a.seq = layout_of(p);
+  a.q = q;
+  a.kv = kv;
+  a.lse = lse;
+  a.scores = scores;
+  a.ld_scores = ld_scores;
+  a.idx = topk_idx;
+  a.loss = loss;
+  a.grad = grad;
+  a.ld_grad = ld_grad;
+  a.heads = p->heads;
+  a.d_latent = p->d_latent;
+  a.d_rope = p->d_rope;
+  a.k = p->topk;
+  a.scale = p->softmax_scale;
+  return hip_status(dsa::launch_align_loss(a, static_cast<hipStream_t>(stream)),
+                    "alignment loss launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_indexer_align_loss(const dsa_problem *p, const uint16_t *q, const uint16_t *kv,
+                                  const float *lse, const float *scores, int64_t ld_scores,
+                                  const int32_t *topk_idx, float *loss, float *grad,
+                                  int64_t ld_grad, void *stream) {
+  return align_impl(p, q, kv, lse, scores, ld_scores, topk_idx, loss, grad, ld_grad, stream);
+}
+
+}  // extern "C"

@@ -65,7 +65,26 @@ struct AttnArgs {
   int32_t nsplit;    // workgroups per token (set by the launcher)
 };
 
+// Indexer alignment loss: idx == nullptr selects the dense warm-up form (all
+// causal keys); grad rows are ld_grad apart (dense: by key position; sparse:
+// by entry of idx).
+struct AlignArgs {
+  SeqLayout seq;
+  const uint16_t *q;
+  const uint16_t *kv;
+  const float *lse;
+  const float *scores;
+  int64_t ld_scores;
+  const int32_t *idx;
+  float *loss;
+  float *grad;
+  int64_t ld_grad;
+  int32_t heads, d_latent, d_rope, k;
+  float scale;
+};
+
 hipError_t launch_indexer(const IndexerArgs &a, hipStream_t stream);
+hipError_t launch_align_loss(const AlignArgs &a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs &a, hipStream_t stream);
 hipError_t launch_sparse_attn(const AttnArgs &a, hipStream_t stream);
 size_t sparse_attn_workspace_bytes(const AttnArgs &a);

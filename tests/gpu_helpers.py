@@ -7,6 +7,13 @@ Tolerances (fixed for this path):
 * top-k: bit-identical to the oracle selector run on the GPU's own scores;
 * attention (given identical indices): max-abs <= 2e-2 and relative
   Frobenius error <= 1e-2.
+* alignment loss (given identical scores, indices and the GPU attention's
+  lse): gradient max-abs <= 1e-3 * max|oracle gradient| of the row, and
+  |loss - oracle| <= 1e-4 * max(1, sum_s p_s (|ln p_s| + |ln q_s|)).  The GPU
+  forms the logits from bf16 products with fp32 sums (relative error ~1e-6 of
+  sum |q_d k_d|) and q_s from fp32 scores (relative error ~|I| * 2^-24), so the
+  probabilities carry about 1e-5 relative error; the loss bound is that error
+  times the magnitude of the terms it multiplies, with a 10x margin.
 """
 import numpy as np
 import torch
@@ -17,6 +24,8 @@ from sparse_attention_18_amd import binding as dsa
 INDEXER_REL_TOL = 1e-3
 ATTN_MAX_ABS = 2e-2
 ATTN_REL_F = 1e-2
+ALIGN_GRAD_REL = 1e-3
+ALIGN_LOSS_REL = 1e-4
 
 
 def to_dev(inp, dev="cuda"):
@@ -104,3 +113,53 @@ def make_paged(inp, block_size, seed=0, extra_blocks=5, high_base_rows=0, device
                                                       extra_blocks=extra_blocks,
                                                       high_base_rows=high_base_rows, device=device)
     return dsa.PagedKV(table, block_size, num_blocks, device=device), kc, ksc, kvc
+
+
+def check_align_rows(loss, grad, q, kv, scores, rows, kv0s, kvlens, positions, scale, idx=None):
+    """Oracle alignment loss on the GPU's own scores (and indices) for packed
+    query rows `rows`; kv0s / kvlens give each row's sequence rows in kv.
+    Only the key rows a row uses are copied to the host: the selected ones
+    (sparse form, its indices renumbered to them) or positions 0..pos (dense).
+    Returns (worst gradient error / row max, worst loss error / bound)."""
+    loss_g = loss[rows].cpu().double().numpy()
+    grad_g = grad[rows].cpu().double().numpy()
+    sc = scores[rows].cpu().double().numpy()
+    idx_np = idx[rows].cpu().numpy() if idx is not None else None
+    worst_g = worst_l = 0.0
+    for i, r in enumerate(rows):
+        q_row = q[r].cpu().double().numpy()
+        pos = int(positions[i])
+        if idx is None:
+            keys = np.arange(pos + 1)
+            kv_use = kv[kv0s[i]:kv0s[i] + pos + 1].cpu().double().numpy()
+            l_ref, g_ref = oracle.alignment_loss_rows(q_row[None], kv_use, [sc[i]], [pos], scale)
+        else:
+            sel = idx_np[i]
+            ok = (sel >= 0) & (sel < kvlens[i])
+            keys = sel[ok].astype(np.int64)
+            at = torch.as_tensor(kv0s[i] + keys, dtype=torch.long, device=kv.device)
+            kv_use = kv[at].cpu().double().numpy()
+            local = np.full_like(sel, -1)
+            local[ok] = np.arange(keys.size)
+            # the oracle reads scores by key row: give it this row's scores in that order
+            l_ref, g_ref = oracle.alignment_loss_rows(q_row[None], kv_use, [sc[i][keys]], [pos], scale,
+                                                      idx=local[None])
+        g_ref = g_ref[0]
+        g_got = grad_g[i, :len(g_ref)]
+        gmax = max(np.abs(g_ref).max() if g_ref.size else 0.0, 1e-30)
+        gerr = np.abs(g_got - g_ref).max() if g_ref.size else 0.0
+        assert np.isfinite(gerr) and gerr <= ALIGN_GRAD_REL * gmax, \
+            f"row {r}: gradient err {gerr:.3e} > {ALIGN_GRAD_REL} * {gmax:.3e}"
+        bound = 1.0
+        if keys.size:
+            p = oracle.attention_target_row(q_row, kv_use, np.arange(keys.size), scale)
+            s_k = sc[i][keys]
+            log_q = s_k - (s_k.max() + np.log(np.exp(s_k - s_k.max()).sum()))
+            nz = p > 0
+            bound = max(1.0, float(np.sum(p[nz] * (np.abs(np.log(p[nz])) + np.abs(log_q[nz])))))
+        lerr = abs(loss_g[i] - l_ref[0])
+        assert np.isfinite(loss_g[i]) and lerr <= ALIGN_LOSS_REL * bound, \
+            f"row {r}: loss {loss_g[i]:.6e} vs {l_ref[0]:.6e} (bound {ALIGN_LOSS_REL * bound:.3e})"
+        worst_g = max(worst_g, gerr / gmax)
+        worst_l = max(worst_l, lerr / bound)
+    return worst_g, worst_l

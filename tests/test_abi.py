@@ -201,3 +201,31 @@ def test_paged_attention_lifts_the_packed_row_bound():
     assert lib.dsa_sparse_attn_paged(ctypes.byref(p), ctypes.byref(g), FAKE, FAKE, None, FAKE, None,
                                      None, 0, None) == binding.DSA_ERR_INVALID_ARGUMENT
     assert "topk_idx" in _msg()
+
+
+def _align(p, lse=FAKE, scores=FAKE, idx=FAKE, loss=FAKE, grad=FAKE, ld=4096, ld_grad=2048):
+    lib = binding.load_library()
+    return lib.dsa_indexer_align_loss(ctypes.byref(p), FAKE, FAKE, lse, scores, ld, idx, loss, grad,
+                                      ld_grad, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(lse=None), binding.DSA_ERR_INVALID_ARGUMENT, "lse"),
+    (dict(scores=FAKE + 4), binding.DSA_ERR_INVALID_ARGUMENT, "scores"),
+    (dict(loss=None), binding.DSA_ERR_INVALID_ARGUMENT, "loss"),
+    (dict(grad=None), binding.DSA_ERR_INVALID_ARGUMENT, "grad"),
+    (dict(idx=FAKE + 4), binding.DSA_ERR_INVALID_ARGUMENT, "topk_idx"),
+    (dict(ld=4000), binding.DSA_ERR_INVALID_ARGUMENT, "ld_scores"),
+    (dict(ld_grad=2047), binding.DSA_ERR_INVALID_ARGUMENT, "ld_grad"),
+    (dict(idx=None, ld_grad=4095), binding.DSA_ERR_INVALID_ARGUMENT, "max_kv_len"),
+])
+def test_align_loss_rejects_bad_arguments(kw, status, needle):
+    assert _align(_problem(), **kw) == status
+    assert needle in _msg()
+
+
+def test_align_loss_shares_the_attention_shape_checks():
+    assert _align(_problem(heads=129)) == binding.DSA_ERR_UNSUPPORTED
+    assert _align(_problem(max_kv_len=3728271, total_kv=3728271), ld=3728272,
+                  idx=None, ld_grad=3728272) == binding.DSA_ERR_UNSUPPORTED
+    assert "max_kv_len" in _msg()
