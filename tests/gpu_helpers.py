@@ -8,12 +8,13 @@ Tolerances (fixed for this path):
 * attention (given identical indices): max-abs <= 2e-2 and relative
   Frobenius error <= 1e-2.
 * alignment loss (given identical scores, indices and the GPU attention's
-  lse): gradient max-abs <= 1e-3 * max|oracle gradient| of the row, and
+  lse): gradient max-abs <= 1e-4 * max_s (p_s + q_s) of the row, and
   |loss - oracle| <= 1e-4 * max(1, sum_s p_s (|ln p_s| + |ln q_s|)).  The GPU
   forms the logits from bf16 products with fp32 sums (relative error ~1e-6 of
   sum |q_d k_d|) and q_s from fp32 scores (relative error ~|I| * 2^-24), so the
-  probabilities carry about 1e-5 relative error; the loss bound is that error
-  times the magnitude of the terms it multiplies, with a 10x margin.
+  probabilities p_s and q_s carry about 1e-5 relative error; the gradient
+  q_s - p_s then errs by about 1e-5 (p_s + q_s), and the loss by that error
+  times the log terms it multiplies: both bounds leave a 5-10x margin.
 """
 import numpy as np
 import torch
@@ -24,7 +25,7 @@ from sparse_attention_18_amd import binding as dsa
 INDEXER_REL_TOL = 1e-3
 ATTN_MAX_ABS = 2e-2
 ATTN_REL_F = 1e-2
-ALIGN_GRAD_REL = 1e-3
+ALIGN_GRAD_REL = 1e-4
 ALIGN_LOSS_REL = 1e-4
 
 
@@ -120,7 +121,7 @@ def check_align_rows(loss, grad, q, kv, scores, rows, kv0s, kvlens, positions, s
     query rows `rows`; kv0s / kvlens give each row's sequence rows in kv.
     Only the key rows a row uses are copied to the host: the selected ones
     (sparse form, its indices renumbered to them) or positions 0..pos (dense).
-    Returns (worst gradient error / row max, worst loss error / bound)."""
+    Returns (worst gradient error / max(p + q), worst loss error / bound)."""
     loss_g = loss[rows].cpu().double().numpy()
     grad_g = grad[rows].cpu().double().numpy()
     sc = scores[rows].cpu().double().numpy()
@@ -146,20 +147,20 @@ def check_align_rows(loss, grad, q, kv, scores, rows, kv0s, kvlens, positions, s
                                                       idx=local[None])
         g_ref = g_ref[0]
         g_got = grad_g[i, :len(g_ref)]
-        gmax = max(np.abs(g_ref).max() if g_ref.size else 0.0, 1e-30)
-        gerr = np.abs(g_got - g_ref).max() if g_ref.size else 0.0
-        assert np.isfinite(gerr) and gerr <= ALIGN_GRAD_REL * gmax, \
-            f"row {r}: gradient err {gerr:.3e} > {ALIGN_GRAD_REL} * {gmax:.3e}"
-        bound = 1.0
+        bound, pq = 1.0, 1.0
         if keys.size:
             p = oracle.attention_target_row(q_row, kv_use, np.arange(keys.size), scale)
             s_k = sc[i][keys]
             log_q = s_k - (s_k.max() + np.log(np.exp(s_k - s_k.max()).sum()))
             nz = p > 0
             bound = max(1.0, float(np.sum(p[nz] * (np.abs(np.log(p[nz])) + np.abs(log_q[nz])))))
+            pq = float((p + np.exp(log_q)).max())
+        gerr = np.abs(g_got - g_ref).max() if g_ref.size else 0.0
+        assert np.isfinite(gerr) and gerr <= ALIGN_GRAD_REL * pq, \
+            f"row {r}: gradient err {gerr:.3e} > {ALIGN_GRAD_REL} * max(p + q) {pq:.3e}"
         lerr = abs(loss_g[i] - l_ref[0])
         assert np.isfinite(loss_g[i]) and lerr <= ALIGN_LOSS_REL * bound, \
             f"row {r}: loss {loss_g[i]:.6e} vs {l_ref[0]:.6e} (bound {ALIGN_LOSS_REL * bound:.3e})"
-        worst_g = max(worst_g, gerr / gmax)
+        worst_g = max(worst_g, gerr / pq)
         worst_l = max(worst_l, lerr / bound)
     return worst_g, worst_l
