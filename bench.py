@@ -8,7 +8,9 @@ selector and the sparse MLA attention against its full causal prefix
 already resident in HBM.  The same run also times the decode step (64
 sequences, cached contexts uniform in [8K, 128K]) and reports it as
 ``decode_us_per_step``, and the same decode step over paged caches (64-row
-blocks, shuffled) as ``decode_paged_us_per_step``.
+blocks, shuffled) as ``decode_paged_us_per_step``.  ``train_align`` times the
+sparse-stage training step: the same 32 chunks, each followed by the indexer
+alignment loss over its selected keys (loss and score gradient per row).
 
 Per-stage durations come from HIP events recorded around each stage call on
 the stream the kernels run on.  ``roofline`` covers the dominant stage:
@@ -18,7 +20,8 @@ published peaks (HBM 8 TB/s, dense FP8 5.0 PFLOP/s, dense bf16 2.5 PFLOP/s).
 the same workload, on the host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode]
-                       [--no-cpu-baseline] [--cpu-rows R] [--stages-json PATH]
+                       [--no-train] [--no-cpu-baseline] [--cpu-rows R]
+                       [--stages-json PATH]
 """
 from __future__ import annotations
 
@@ -49,9 +52,10 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-_KERNEL_SOURCES = {"sparse_attn": ["sparse_attn.hip", "common.h", "launch.h"],
+_KERNEL_SOURCES = {"sparse_attn": ["sparse_attn.hip", "kv_gather.h", "common.h", "launch.h"],
                    "indexer": ["indexer.hip", "common.h", "launch.h"],
-                   "topk": ["topk.hip", "common.h", "launch.h"]}
+                   "topk": ["topk.hip", "common.h", "launch.h"],
+                   "align_loss": ["align.hip", "kv_gather.h", "common.h", "launch.h"]}
 
 
 def measured_traffic(stage: str):
@@ -99,6 +103,20 @@ def attn_flops(wl, positions):
     return float(m.sum()) * 2.0 * wl.heads * (wl.d_qk + wl.d_latent)
 
 
+def align_bytes(wl, positions):
+    """Alignment loss, per selected pair: the latent KV row (1152 B), its index,
+    its score and its gradient (4 B each); per token: q (H x 576 bf16), lse
+    (H floats) and the loss."""
+    m = np.minimum(np.asarray(positions, dtype=np.float64) + 1, wl.topk)
+    per_tok = wl.heads * wl.d_qk * 2 + wl.heads * 4 + 4
+    return float(m.sum()) * (wl.d_qk * 2 + 12) + per_tok * len(m)
+
+
+def align_flops(wl, positions):
+    m = np.minimum(np.asarray(positions, dtype=np.float64) + 1, wl.topk)
+    return float(m.sum()) * 2.0 * wl.heads * wl.d_qk
+
+
 # ----------------------------------------------------------------- prefill step
 class ChunkedPrefill:
     def __init__(self, wl, dev):
@@ -139,6 +157,29 @@ class ChunkedPrefill:
                             self.out[sl], self.lse[sl])
             if events is not None:
                 events[ci][3].record()
+
+    def train_step(self, events=None):
+        """The forward chunks, each followed by the indexer alignment loss over
+        its selected keys (while the chunk's scores are still in place)."""
+        inp, wl = self.inp, self.wl
+        if not hasattr(self, "grad"):
+            self.grad = torch.empty(wl.chunk, wl.topk, dtype=torch.float32, device=self.scores.device)
+            self.loss = torch.empty(wl.seq_len, dtype=torch.float32, device=self.scores.device)
+        for ci, (r0, sl, prob) in enumerate(self.chunks):
+            rows = sl.stop - sl.start
+            scores = self.scores[:rows]
+            dsa.indexer_scores(prob, inp["q_fp8"][sl], inp["q_scale"][sl], inp["w"][sl],
+                               inp["k_fp8"][: sl.stop], inp["k_scale"][: sl.stop],
+                               scores, self.ld)
+            dsa.topk(prob, scores, self.idx[sl], ld=self.ld)
+            dsa.sparse_attn(prob, inp["q"][sl], inp["kv"][: sl.stop], self.idx[sl],
+                            self.out[sl], self.lse[sl])
+            if events is not None:
+                events[ci][0].record()
+            dsa.indexer_align_loss(prob, inp["q"][sl], inp["kv"][: sl.stop], self.lse[sl], scores,
+                                   self.loss[sl], self.grad[:rows], idx=self.idx[sl], ld=self.ld)
+            if events is not None:
+                events[ci][1].record()
 
 
 def run_prefill(args, dev):
@@ -204,6 +245,37 @@ def run_prefill(args, dev):
     ms_per_step = gpu_ms / args.steps
     value = wl.seq_len / (ms_per_step * 1e-3)
     return bench, wl, value, ms_per_step, stages, per_chunk
+
+
+def run_train(bench, steps=2):
+    """Sparse-stage training step: forward chunks plus the alignment loss."""
+    wl = bench.wl
+    bench.train_step()
+    torch.cuda.synchronize()
+    nch = len(bench.chunks)
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nch)]
+           for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for s in range(steps):
+        bench.train_step(evs[s])
+    end.record()
+    torch.cuda.synchronize()
+    step_ms = start.elapsed_time(end) / steps
+    loss_ms = sum(e[0].elapsed_time(e[1]) for st in evs for e in st) / steps
+    pos = bench.positions
+    t = loss_ms * 1e-3
+    rate = align_bytes(wl, pos) / t
+    log(f"[bench] training step {step_ms:.1f} ms, alignment loss {loss_ms:.2f} ms")
+    return {"ms_per_step": round(loss_ms, 3), "launches_per_step": nch,
+            "avg_launch_us": round(loss_ms / nch * 1e3, 1), "bound": "hbm",
+            "achieved": round(rate / 1e9, 1), "peak": round(HBM_PEAK / 1e9, 1), "unit": "GB/s",
+            "frac": round(rate / HBM_PEAK, 4),
+            "bf16_tflops": round(align_flops(wl, pos) / t / 1e12, 1),
+            "traffic": measured_traffic("align_loss"),
+            "train_step_ms": round(step_ms, 3),
+            "train_tokens_per_s": round(wl.seq_len / (step_ms * 1e-3), 1),
+            "steps": steps}
 
 
 def run_decode(args, dev):
@@ -300,6 +372,7 @@ def main():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-train", action="store_true", help="skip the alignment-loss training step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--stages-json", default=None, help="also write per-chunk stage times here")
@@ -332,6 +405,9 @@ def main():
     roofline = {"bound": d["bound"], "achieved": d["achieved"], "peak": d["peak"],
                 "unit": d["unit"], "frac": d["frac"], "traffic": traffic, "kernel": dominant,
                 "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)"}
+    train = None
+    if not args.no_train:
+        train = run_train(bench)
     decode_us = decode_paged_us = None
     if not args.no_decode:
         decode_us, decode_paged_us, _ = run_decode(args, dev)
@@ -356,6 +432,7 @@ def main():
                           "ctx": [wk.DECODE_B64.ctx_min, wk.DECODE_B64.ctx_max]},
         "roofline": roofline,
         "stages": stages,
+        "train_align": train,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
