@@ -30,7 +30,8 @@ What it computes, stage by stage, in the order the pages give:
    with a KL loss towards the attention's distribution, over all causal keys
    in the dense warm-up and over the selected keys afterwards.  The loss of a
    token is KL(head-summed, L1-normalised attention probabilities || softmax
-   of the indexer scores), with its gradient taken with respect to the scores.
+   of the indexer scores), with its gradient taken with respect to the scores,
+   and that gradient carried back through the indexer to q, w and k.
 
 Readings where the pages are silent or garbled (each listed in the design doc):
 the indexer formula and FP8 format; causality (a key is visible iff its
@@ -248,3 +249,56 @@ def alignment_loss_rows(q_attn, kv, scores, pos, scale: float, idx=None):
             full[np.asarray(idx[r]) >= 0] = g
             grads.append(full)
     return np.array(losses), grads
+
+
+# ---------------------------------------------------------------------------
+# Stage 4b (training): backward of the lightning indexer
+# ---------------------------------------------------------------------------
+# The alignment loss's gradient on the scores flows into the indexer's inputs
+# (same section of the ivugangingo.com article: only the indexer learns from
+# that loss).  With the score of stage 1,
+#     score(t, s) = sum_j w[t, j] * ReLU(z[t, j, s]),   z = q[t, j] . k[s]
+# (q and k dequantised), and an upstream gradient g[t, s], the chain rule
+# gives, taking the ReLU's derivative at 0 as 0:
+#     dw[t, j] = sum_s g[t, s] * ReLU(z[t, j, s])
+#     dq[t, j] = sum_s g[t, s] * w[t, j] * [z[t, j, s] > 0] * k[s]
+#     dk[s]    = sum_t sum_j g[t, s] * w[t, j] * [z[t, j, s] > 0] * q[t, j]
+def indexer_backward_row(q_row, w_row, keys, g):
+    """Gradients of sum_i g[i] * score(keys[i]) for one query row.
+
+    q_row [H_I, d_I], w_row [H_I], keys [m, d_I] (dequantised float64), g [m].
+    Returns (dq [H_I, d_I], dw [H_I], dk [m, d_I]); dk[i] belongs to keys[i].
+    """
+    z = q_row @ keys.T                          # [H_I, m]
+    dw = np.maximum(z, 0.0) @ g
+    e = (z > 0) * w_row[:, None] * g[None, :]   # d score_i / d z[j, i], times g[i]
+    return e @ keys, dw, e.T @ q_row
+
+
+def indexer_backward_rows(q, w, k, pos, grads, idx=None):
+    """Indexer backward for a set of query rows of one sequence, in float64.
+
+    q [R, H_I, d_I], w [R, H_I], k [S, d_I] dequantised; pos [R].  grads are
+    the upstream gradients on the scores: dense (idx None), row r is indexed
+    by key position 0..pos[r]; sparse, row r is aligned with idx[r] (entries
+    with idx -1 ignored).  Returns (dq [R, H_I, d_I], dw [R, H_I], dk [S, d_I]),
+    dk summed over the rows.
+    """
+    R = len(pos)
+    dq = np.zeros(q.shape)
+    dw = np.zeros(w.shape)
+    dk = np.zeros(k.shape)
+    for r in range(R):
+        g_row = np.asarray(grads[r], dtype=np.float64)
+        if idx is None:
+            keys = np.arange(int(pos[r]) + 1)
+            g = g_row[: keys.size]
+        else:
+            sel = np.asarray(idx[r])
+            ok = sel >= 0
+            keys, g = sel[ok], g_row[: sel.size][ok]
+        if keys.size == 0:
+            continue
+        dq[r], dw[r], dk_rows = indexer_backward_row(q[r], w[r], k[keys], g)
+        np.add.at(dk, keys, dk_rows)
+    return dq, dw, dk
