@@ -240,6 +240,38 @@ dsa_status dsa_indexer_align_loss(const dsa_problem *p, const uint16_t *q, const
                                   const int32_t *topk_idx, float *loss, float *grad,
                                   int64_t ld_grad, void *stream);
 
+/*
+ * Backward of the lightning indexer (training): carries a gradient on the
+ * scores -- the alignment loss's grad above -- back to the indexer's inputs
+ * (the ivugangingo.com article, "DeepSeek sparse attention pre-training
+ * continues": the indexer is what that loss trains).  With q~ = q_scale * q8
+ * and k~ = k_scale * k8 the dequantised values, z[j, s] = q~[r, j] . k~[s],
+ * and G[r, s] the given gradient over row r's keys K_r (dense: positions
+ * 0..pos(r); sparse: the valid entries of topk_idx[r]):
+ *   dw[r, j]     = sum_{s in K_r} G[r, s] * ReLU(z[j, s])
+ *   dq[r, j, :]  = sum_{s in K_r} G[r, s] * w[r, j] * [z[j, s] > 0] * k~[s, :]
+ *   dk[b, s, :] += sum_{r of b} sum_j G[r, s] * w[r, j] * [z[j, s] > 0] * q~[r, j, :]
+ * (the ReLU's derivative at 0 is taken as 0).  dq and dw are gradients with
+ * respect to the dequantised q~ and w and are overwritten; dk, with respect
+ * to k~, is ADDED to (a key is shared by many rows and, in a chunked
+ * prefill, by several calls), in an order that varies from run to run, so
+ * the caller zeroes it once per step.
+ *   q_fp8, q_scale, w, k_fp8, k_scale as for dsa_indexer_scores
+ *   topk_idx [total_q, k] int32, or NULL for the dense form
+ *   grad: sparse [total_q, ld_grad] aligned with topk_idx (ld_grad >= k);
+ *         dense [total_q, ld_grad] by position (ld_grad >= max_kv_len)
+ *   dq [total_q, H_I, d_I] float   dw [total_q, H_I] float   dk [total_kv, d_I] float
+ * The (H_I, d_I) = (64, 128) shape runs on MFMA: the mask is decided on the
+ * fp32 dot product of the exact e4m3 values and the products use bf16
+ * operands with the gradient split into two bf16 terms (about 2^-17
+ * relative), fp32 accumulation.  Other shapes take a plain fp32 path.  dk
+ * must be ordinary device memory (hipMalloc): fp32 atomics add to it.
+ */
+dsa_status dsa_indexer_backward(const dsa_problem *p, const uint8_t *q_fp8, const float *q_scale,
+                                const float *w, const uint8_t *k_fp8, const float *k_scale,
+                                const int32_t *topk_idx, const float *grad, int64_t ld_grad,
+                                float *dq, float *dw, float *dk, void *stream);
+
 /* Bytes of device workspace the given entry point needs for problem p
  * (which = DSA_WS_TOPK, DSA_WS_ATTN or DSA_WS_FORWARD); 0 if none.  Returns
  * (size_t)-1 for an invalid problem (see dsa_last_error).  The paged entry

@@ -27,7 +27,7 @@ WS_TOPK, WS_ATTN, WS_FORWARD = 0, 1, 2
 
 EXPORTED = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward",
             "dsa_indexer_scores_paged", "dsa_sparse_attn_paged", "dsa_forward_paged",
-            "dsa_indexer_align_loss", "dsa_workspace_bytes", "dsa_last_error", "dsa_version")
+            "dsa_indexer_align_loss", "dsa_indexer_backward", "dsa_workspace_bytes", "dsa_last_error", "dsa_version")
 
 
 class DsaLibraryError(RuntimeError):
@@ -103,9 +103,10 @@ def load_library():
         lib.dsa_sparse_attn_paged.argtypes = [P, G, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.dsa_forward_paged.argtypes = [P, G, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.dsa_indexer_align_loss.argtypes = [P, vp, vp, vp, vp, i64, vp, vp, vp, i64, vp]
+        lib.dsa_indexer_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp]
         for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward",
                      "dsa_indexer_scores_paged", "dsa_sparse_attn_paged", "dsa_forward_paged",
-                     "dsa_indexer_align_loss"):
+                     "dsa_indexer_align_loss", "dsa_indexer_backward"):
             getattr(lib, name).restype = ctypes.c_int
         lib.dsa_workspace_bytes.argtypes = [P, ctypes.c_int]
         lib.dsa_workspace_bytes.restype = sz
@@ -300,6 +301,31 @@ def indexer_align_loss(prob: Problem, q, kv, lse, scores, loss, grad, idx=None, 
         _ptr(idx, torch.int32, "idx", (c.total_q, c.topk)),
         _ptr(loss, torch.float32, "loss", (c.total_q,)),
         _ptr(grad, torch.float32, "grad", (c.total_q, ld_grad)), ld_grad, _stream(stream)))
+
+
+def indexer_backward(prob: Problem, q_fp8, q_scale, w, k_fp8, k_scale, grad, dq, dw, dk, idx=None,
+                     stream=None):
+    """dsa_indexer_backward: the score gradient ``grad`` carried to dq [total_q, H_I,
+    d_I], dw [total_q, H_I] (both overwritten) and dk [total_kv, d_I] (added to).
+
+    Sparse form (``idx`` given): grad is aligned with idx; dense form (``idx``
+    None): grad is by position, grad.shape[1] >= max_kv_len."""
+    c = prob.c
+    if not isinstance(grad, torch.Tensor) or grad.dim() != 2:
+        raise ValueError("grad must be a 2-D tensor")
+    ld_grad = int(grad.shape[1])
+    _check(load_library().dsa_indexer_backward(
+        ctypes.byref(c),
+        _ptr(q_fp8, torch.uint8, "q_fp8", (c.total_q, c.idx_heads, c.idx_dim)),
+        _ptr(q_scale, torch.float32, "q_scale", (c.total_q,)),
+        _ptr(w, torch.float32, "w", (c.total_q, c.idx_heads)),
+        _ptr(k_fp8, torch.uint8, "k_fp8", (c.total_kv, c.idx_dim)),
+        _ptr(k_scale, torch.float32, "k_scale", (c.total_kv,)),
+        _ptr(idx, torch.int32, "idx", (c.total_q, c.topk)),
+        _ptr(grad, torch.float32, "grad", (c.total_q, ld_grad)), ld_grad,
+        _ptr(dq, torch.float32, "dq", (c.total_q, c.idx_heads, c.idx_dim)),
+        _ptr(dw, torch.float32, "dw", (c.total_q, c.idx_heads)),
+        _ptr(dk, torch.float32, "dk", (c.total_kv, c.idx_dim)), _stream(stream)))
 
 
 class PagedKV:

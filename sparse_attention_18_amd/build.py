@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libdsa.so")
 ROOT = os.path.dirname(PKG)
 
 ARCH = "gfx950"
-SOURCES = ["indexer.hip", "topk.hip", "sparse_attn.hip", "align.hip", "abi.cpp"]
+SOURCES = ["indexer.hip", "topk.hip", "sparse_attn.hip", "align.hip", "indexer_bwd.hip", "abi.cpp"]
 # Packed-FP32 VALU forms are kept out of every device code object.
 # IEEE mode is off (no NaN quieting on min/max): the kernels never rely on
 # signalling-NaN behaviour, and fmaxf then lowers to a single v_max_f32.

@@ -484,3 +484,59 @@ dsa_status dsa_indexer_align_loss(const dsa_problem *p, const uint16_t *q, const
 }
 
 }  // extern "C"
+
+namespace {
+
+dsa_status indexer_bwd_impl(const dsa_problem *p, const uint8_t *q_fp8, const float *q_scale,
+                            const float *w, const uint8_t *k_fp8, const float *k_scale,
+                            const int32_t *topk_idx, const float *grad, int64_t ld_grad, float *dq,
+                            float *dw, float *dk, void *stream) {
+  DSA_TRY(check_problem(p));
+  DSA_TRY(check_indexer_dims(p));
+  DSA_TRY(check_indexer_ptrs(p, q_fp8, q_scale, w, k_fp8, k_scale));
+  const bool hq = p->total_q > 0;
+  DSA_TRY(check_ptr(grad, hq, "grad"));
+  DSA_TRY(check_ptr(dq, hq, "dq"));
+  DSA_TRY(check_ptr(dw, hq, "dw"));
+  DSA_TRY(check_ptr(dk, p->total_kv > 0, "dk"));
+  if (topk_idx != nullptr) DSA_TRY(check_ptr(topk_idx, hq, "topk_idx"));
+  const int64_t need = topk_idx != nullptr ? (int64_t)p->topk : p->max_kv_len;
+  DSA_CHECK(ld_grad >= need && ld_grad >= 1, DSA_ERR_INVALID_ARGUMENT,
+            "ld_grad (%lld) must be >= %s (%lld) and >= 1", (long long)ld_grad,
+            topk_idx != nullptr ? "topk" : "max_kv_len", (long long)need);
+  DSA_CHECK(p->total_q == 0 || ld_grad <= INT64_MAX / 4 / p->total_q, DSA_ERR_INVALID_ARGUMENT,
+            "grad matrix size overflows");
+  DSA_CHECK(p->max_kv_len <= INT32_MAX, DSA_ERR_UNSUPPORTED, "max_kv_len must fit int32");
+  dsa::IndexerBwdArgs a;
+  a.seq = layout_of(p);
+  a.q_fp8 = q_fp8;
+  a.q_scale = q_scale;
+  a.w = w;
+  a.k_fp8 = k_fp8;
+  a.k_scale = k_scale;
+  a.idx = topk_idx;
+  a.grad = grad;
+  a.ld_grad = ld_grad;
+  a.dq = dq;
+  a.dw = dw;
+  a.dk = dk;
+  a.idx_heads = p->idx_heads;
+  a.idx_dim = p->idx_dim;
+  a.k = p->topk;
+  return hip_status(dsa::launch_indexer_backward(a, static_cast<hipStream_t>(stream)),
+                    "indexer backward launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_indexer_backward(const dsa_problem *p, const uint8_t *q_fp8, const float *q_scale,
+                                const float *w, const uint8_t *k_fp8, const float *k_scale,
+                                const int32_t *topk_idx, const float *grad, int64_t ld_grad,
+                                float *dq, float *dw, float *dk, void *stream) {
+  return indexer_bwd_impl(p, q_fp8, q_scale, w, k_fp8, k_scale, topk_idx, grad, ld_grad, dq, dw,
+                          dk, stream);
+}
+
+}  // extern "C"

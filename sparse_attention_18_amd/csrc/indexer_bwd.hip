@@ -1,0 +1,462 @@
+// Backward of the lightning indexer (training) for gfx950.
+//
+// The method (ivugangingo.com article on DeepSeek-V3.2, section "DeepSeek
+// sparse attention pre-training continues"): the indexer is the part the
+// alignment loss trains.  Given that loss's gradient g[t, s] on the scores,
+// the chain rule through
+//     score(t, s) = sum_j w[t, j] * ReLU(z[t, j, s]),   z = q~[t, j] . k~[s]
+// (q~ = q_scale * q8 and k~ = k_scale * k8 dequantised; the ReLU's derivative
+// at 0 taken as 0) gives, over the token's keys (its selected set, or every
+// causal key in the dense warm-up form):
+//     dw[t, j]   = sum_s g[t, s] * ReLU(z[t, j, s])
+//     dq~[t, j]  = sum_s E[j, s] * k8[s],      E[j, s] = g[t, s] * w[t, j] * k_scale[s] * [z > 0]
+//     dk~[s]    += (q_scale[t] / k_scale[s]) * sum_j E[j, s] * q8[t, j]
+//
+// MFMA path (H_I = 64, d_I = 128): one workgroup of 4 waves per token; keys
+// in 64-key tiles, double-buffered in LDS as in the prefill indexer.
+//  * z on v_mfma_f32_16x16x128_f8f6f4 straight from the FP8 bytes (wave w:
+//    keys 16w..16w+15, all 64 heads), so the ReLU mask is decided on the
+//    fp32 dot product of the exact e4m3 values.
+//  * E is formed in fp32 and split into two bf16 terms (hi + lo carries it to
+//    about 2^-17); e4m3 values are exact in bf16.  dq~ = E . K8 and the
+//    tile's dk~ block = E^T . Q8 run on v_mfma_f32_16x16x32_bf16 (a hi and a
+//    lo product each) with fp32 accumulation: wave w owns heads 16w.. of dq
+//    (all 128 dims, in registers across the tiles) and keys 16w.. of each
+//    tile's dk block.
+//  * dq contracts over keys and dk over heads, so E goes to LDS twice
+//    (head-major and key-major), each key tile is transposed once into bf16
+//    (dims x keys), and Q8's transpose is built once per token.
+//  * A key is selected by many queries, so dk rows of different tokens
+//    collide: each tile's block is added to dk with fp32 atomics.
+#include "common.h"
+#include "launch.h"
+
+namespace dsa {
+namespace {
+
+constexpr int kBT = 256;        // threads per workgroup
+constexpr int kBKeys = 64;      // keys per tile
+constexpr int kBMaxK = 4096;
+
+// Byte offset of 16-byte chunk j (of 8) of row n in a tile of 128-byte fp8
+// rows; chunks are XOR-swizzled by (n >> 1) & 7 as in the forward indexer.
+__device__ __forceinline__ int f8_off(int n, int j) { return n * 128 + 16 * (j ^ ((n >> 1) & 7)); }
+
+// Byte offset of bf16 element c of row r in an array of 64-element (128-byte)
+// rows; the 16-byte chunks of row r are XOR-swizzled by r & 7, so 16 lanes
+// reading the same chunk of 16 consecutive rows spread over the banks.
+__device__ __forceinline__ int b16_off(int r, int c) {
+  return r * 128 + ((((c >> 3) ^ r) & 7) << 4) + (c & 7) * 2;
+}
+
+// bf16 bits of a float that is exactly representable (an e4m3 value).
+__device__ __forceinline__ uint32_t top16(float f) { return __float_as_uint(f) >> 16; }
+
+// Transpose a [64 rows][128 dims] fp8 tile (f8_off layout) into bf16
+// [128 dims][64 rows] (b16_off layout).  Thread: rows 4rg..4rg+3, dims
+// 8dg..8dg+7; four 8-byte reads, eight 8-byte writes.
+__device__ __forceinline__ void transpose_f8_bf16(const DSA_LDS uint8_t *src, DSA_LDS uint8_t *dst, int tid) {
+  const int rg = tid & 15, dg = tid >> 4;
+  float f[4][8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const v2i x = *reinterpret_cast<const DSA_LDS v2i *>(src + f8_off(4 * rg + i, dg >> 1) + 8 * (dg & 1));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)x[h], 1.0f, false);
+      const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((uint32_t)x[h], 1.0f, true);
+      f[i][4 * h + 0] = lo[0];
+      f[i][4 * h + 1] = lo[1];
+      f[i][4 * h + 2] = hi[0];
+      f[i][4 * h + 3] = hi[1];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const uint32_t a = top16(f[0][e]) | (top16(f[1][e]) << 16);
+    const uint32_t b = top16(f[2][e]) | (top16(f[3][e]) << 16);
+    *reinterpret_cast<DSA_LDS v2i *>(dst + b16_off(8 * dg + e, 4 * rg)) = v2i{(int)a, (int)b};
+  }
+}
+
+__device__ __forceinline__ v8bf lds_v8bf(const DSA_LDS uint8_t *p) {
+  return __builtin_bit_cast(v8bf, *reinterpret_cast<const DSA_LDS v4i *>(p));
+}
+
+template <bool kDense>
+__global__ __launch_bounds__(kBT) void indexer_bwd_kernel(IndexerBwdArgs p) {
+  constexpr int H = 64, D = 128;
+  __shared__ __attribute__((aligned(16))) uint8_t ktile[2][kBKeys * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t kT[D * 128];          // bf16 [dims][64]
+  __shared__ __attribute__((aligned(16))) uint8_t eh[2][H * 128];       // bf16 [heads][keys]: hi, lo
+  __shared__ __attribute__((aligned(16))) uint8_t et[2][kBKeys * 128];  // bf16 [keys][heads]: hi, lo
+  __shared__ float tks[2][kBKeys], tg[2][kBKeys];
+  __shared__ int tpos[2][kBKeys];
+  __shared__ int idxl[kDense ? 1 : kBMaxK];
+  __shared__ uint16_t slotl[kDense ? 1 : kBMaxK];
+  __shared__ int s_scan[4];
+  __shared__ float sdw[4][H];
+
+  const int64_t t = __builtin_amdgcn_workgroup_id_x();
+  const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int k = p.k;
+
+  SeqInfo s;
+  row_seq(p.seq, t, s);
+  const bool row_ok = t >= s.q0 && t < s.q1;
+  const float qsc = p.q_scale[t];
+  const float *grow = p.grad + t * p.ld_grad;
+
+  // z operands (A of 16x16x128): head hb*16 + r16, dims 32*g4 .. +31.
+  v8i qa[4];
+  float wv[4][4];   // w of this lane's result heads hb*16 + 4*g4 + j
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb) {
+    const v4i *src = reinterpret_cast<const v4i *>(p.q_fp8 + (t * H + hb * 16 + r16) * (int64_t)D + 32 * g4);
+    const v4i lo = src[0], hi = src[1];
+    qa[hb] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wv[hb][j] = p.w[t * H + hb * 16 + 4 * g4 + j];
+  }
+
+  // Key set: m keys; sparse, compacted with their entry slots.
+  int m;
+  if constexpr (!kDense) {
+    constexpr int per = kBMaxK / kBT;
+    const int32_t *irow = p.idx + t * k;
+    const int i0 = tid * per;
+    int vals[per];
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < per; ++e) {
+      const int i = i0 + e;
+      int v = -1;
+      if (row_ok && i < k) v = irow[i];
+      vals[e] = (v >= 0 && v < s.kvlen) ? v : -1;
+      cnt += vals[e] >= 0;
+    }
+    const int inc = (int)wave_scan<0>((uint32_t)cnt);
+    if (lane == 63) s_scan[wave] = inc;
+    __syncthreads();
+    int base = inc - cnt;
+    m = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) {
+      const int x = s_scan[w2];
+      base += w2 < wave ? x : 0;
+      m += x;
+    }
+#pragma unroll
+    for (int e = 0; e < per; ++e)
+      if (vals[e] >= 0) {
+        idxl[base] = vals[e];
+        slotl[base] = (uint16_t)(i0 + e);
+        ++base;
+      }
+    __syncthreads();
+  } else {
+    m = row_ok ? (int)(row_pos(s, t) + 1) : 0;
+  }
+
+  // Tile staging: each thread carries two 16-byte chunks of the 64 key rows;
+  // threads 0..63 also the key's scale, gradient and position.  Keys past m
+  // get zero bytes and a zero gradient.
+  const uint8_t *kseq = p.k_fp8 + s.kv0 * D;
+  v4i st[2];
+  float st_ks = 0.f, st_g = 0.f;
+  int st_pos = 0;
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int chunk = tid + kBT * e, n = chunk >> 3, j = chunk & 7;
+      const int c = t0 + n;
+      const int cc = c < m ? c : m - 1;
+      const int pos = kDense ? cc : idxl[cc];
+      const v4i x = *reinterpret_cast<const v4i *>(kseq + (int64_t)pos * D + 16 * j);
+      st[e] = c < m ? x : v4i{0, 0, 0, 0};
+    }
+    if (tid < kBKeys) {
+      const int c = t0 + tid;
+      const int cc = c < m ? c : m - 1;
+      st_pos = kDense ? cc : idxl[cc];
+      st_ks = p.k_scale[s.kv0 + st_pos];
+      const float gv = grow[kDense ? cc : (int)slotl[cc]];
+      st_g = c < m ? gv : 0.f;
+    }
+  };
+  auto commit = [&](int buf) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int chunk = tid + kBT * e, n = chunk >> 3, j = chunk & 7;
+      *reinterpret_cast<v4i *>(&ktile[buf][f8_off(n, j)]) = st[e];
+    }
+    if (tid < kBKeys) {
+      tks[buf][tid] = st_ks;
+      tg[buf][tid] = st_g;
+      tpos[buf][tid] = st_pos;
+    }
+  };
+
+  float dw[4][4];
+  v4f dq[8];
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dw[hb][j] = 0.f;
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) dq[nb] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  if (m > 0) {
+    // Q8 transposed to bf16 [dims][heads] (through ktile[1] and kT), then
+    // read once as the dk products' B operands: dim nb*16 + r16, heads
+    // 32*ks + 8*g4 .. +7.
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int chunk = tid + kBT * e, n = chunk >> 3, j = chunk & 7;
+      *reinterpret_cast<v4i *>(&ktile[1][f8_off(n, j)]) =
+          *reinterpret_cast<const v4i *>(p.q_fp8 + (t * H + n) * (int64_t)D + 16 * j);
+    }
+    fetch(0);
+    commit(0);
+    __syncthreads();
+    transpose_f8_bf16((const DSA_LDS uint8_t *)ktile[1], (DSA_LDS uint8_t *)kT, tid);
+    __syncthreads();
+  }
+  v8bf qb[8][2];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      qb[nb][ks] = m > 0 ? lds_v8bf((const DSA_LDS uint8_t *)kT + b16_off(nb * 16 + r16, 32 * ks + 8 * g4))
+                         : v8bf{};
+  __syncthreads();
+
+  const int key_l = 16 * wave + r16;   // this lane's tile key in the z layout
+  float *dkseq = p.dk + s.kv0 * D;
+  int buf = 0;
+  for (int t0 = 0; t0 < m; t0 += kBKeys) {
+    const bool has_next = t0 + kBKeys < m;
+    if (has_next) fetch(t0 + kBKeys);
+    const DSA_LDS uint8_t *kt = (const DSA_LDS uint8_t *)ktile[buf];
+    // z for keys 16*wave + r16 (B: that key's dims 32*g4 .. +31), all heads.
+    v4f z[4];
+    {
+      const v4i lo = *reinterpret_cast<const DSA_LDS v4i *>(kt + f8_off(key_l, 2 * g4));
+      const v4i hi = *reinterpret_cast<const DSA_LDS v4i *>(kt + f8_off(key_l, 2 * g4 + 1));
+      const v8i bop = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+      for (int hb = 0; hb < 4; ++hb) z[hb] = mfma_16x16x128_fp8(qa[hb], bop, v4f{0.f, 0.f, 0.f, 0.f});
+    }
+    const float gk = tg[buf][key_l] * tks[buf][key_l];   // g * k_scale of the lane's key
+    const float cw = gk * qsc;
+#pragma unroll
+    for (int hb = 0; hb < 4; ++hb) {
+      uint32_t hiw[4], low[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float zr = z[hb][j];
+        dw[hb][j] = fmaf(fmaxf(zr, 0.f), cw, dw[hb][j]);
+        const float e = zr > 0.f ? wv[hb][j] * gk : 0.f;
+        hiw[j] = f32_to_bf16_bits(e);
+        low[j] = f32_to_bf16_bits(e - bf16_bits_to_f32(hiw[j]));
+        const int head = hb * 16 + 4 * g4 + j;
+        *reinterpret_cast<uint16_t *>(&eh[0][b16_off(head, key_l)]) = (uint16_t)hiw[j];
+        *reinterpret_cast<uint16_t *>(&eh[1][b16_off(head, key_l)]) = (uint16_t)low[j];
+      }
+      const int c0 = hb * 16 + 4 * g4;
+      *reinterpret_cast<v2i *>(&et[0][b16_off(key_l, c0)]) =
+          v2i{(int)(hiw[0] | (hiw[1] << 16)), (int)(hiw[2] | (hiw[3] << 16))};
+      *reinterpret_cast<v2i *>(&et[1][b16_off(key_l, c0)]) =
+          v2i{(int)(low[0] | (low[1] << 16)), (int)(low[2] | (low[3] << 16))};
+    }
+    transpose_f8_bf16(kt, (DSA_LDS uint8_t *)kT, tid);
+    __syncthreads();
+
+    // dq[heads 16*wave + ...][all dims] += E . K8   (K = the tile's keys)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const v8bf ahi = lds_v8bf((const DSA_LDS uint8_t *)eh[0] + b16_off(16 * wave + r16, 32 * ks + 8 * g4));
+      const v8bf alo = lds_v8bf((const DSA_LDS uint8_t *)eh[1] + b16_off(16 * wave + r16, 32 * ks + 8 * g4));
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const v8bf b = lds_v8bf((const DSA_LDS uint8_t *)kT + b16_off(nb * 16 + r16, 32 * ks + 8 * g4));
+        dq[nb] = mfma_16x16x32_bf16(ahi, b, dq[nb]);
+        dq[nb] = mfma_16x16x32_bf16(alo, b, dq[nb]);
+      }
+    }
+    // dk block[keys 16*wave + ...][all dims] = E^T . Q8   (K = heads)
+    v4f dkb[8];
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) dkb[nb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const v8bf ahi = lds_v8bf((const DSA_LDS uint8_t *)et[0] + b16_off(16 * wave + r16, 32 * ks + 8 * g4));
+      const v8bf alo = lds_v8bf((const DSA_LDS uint8_t *)et[1] + b16_off(16 * wave + r16, 32 * ks + 8 * g4));
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        dkb[nb] = mfma_16x16x32_bf16(ahi, qb[nb][ks], dkb[nb]);
+        dkb[nb] = mfma_16x16x32_bf16(alo, qb[nb][ks], dkb[nb]);
+      }
+    }
+    // element j: key 16*wave + 4*g4 + j, dim nb*16 + r16
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = 16 * wave + 4 * g4 + j;
+      if (t0 + key < m) {
+        const float f = qsc / tks[buf][key];
+        float *drow = dkseq + (int64_t)tpos[buf][key] * D + r16;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) unsafeAtomicAdd(drow + nb * 16, dkb[nb][j] * f);
+      }
+    }
+    if (has_next) commit(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+  }
+
+  // dw: sum over the 16 lanes of a row group (keys), then over the waves.
+#pragma unroll
+  for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float v = dw[hb][j];
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+      if (r16 == 0) sdw[wave][hb * 16 + 4 * g4 + j] = v;
+    }
+  __syncthreads();
+  if (!row_ok) return;
+  if (tid < H) p.dw[t * H + tid] = (sdw[0][tid] + sdw[1][tid]) + (sdw[2][tid] + sdw[3][tid]);
+  // dq: element j of block nb is head 16*wave + 4*g4 + j, dim nb*16 + r16
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float *qrow = p.dq + (t * H + 16 * wave + 4 * g4 + j) * (int64_t)D + r16;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) qrow[nb * 16] = dq[nb][j];
+  }
+}
+
+// Generic path: any H_I <= 128 and d_I <= 128; one workgroup per token,
+// fp32 arithmetic on the dequantised values, keys in chunks of 32.
+constexpr int kSBKeys = 32;
+constexpr int kSBMaxQ = 64;     // dq entries per thread: H_I * d_I <= 128 * 128 = 64 * 256
+
+template <bool kDense>
+__global__ __launch_bounds__(kBT) void small_indexer_bwd_kernel(IndexerBwdArgs p) {
+  __shared__ float qd[128 * 128];           // q~ [H][d]
+  __shared__ float kc[kSBKeys][128];        // k~ of the chunk's keys
+  __shared__ float ec[128][kSBKeys];        // E = g * w * [z > 0]
+  __shared__ float rc[128][kSBKeys];        // g * ReLU(z)
+  __shared__ float gc[kSBKeys];
+  __shared__ int pc[kSBKeys];
+  __shared__ int rows[kDense ? 1 : kBMaxK];
+  __shared__ int nvalid;
+  const int64_t t = blockIdx.x;
+  SeqInfo s;
+  row_seq(p.seq, t, s);
+  if (t < s.q0 || t >= s.q1) return;
+  const int H = p.idx_heads, D = p.idx_dim, k = p.k, tid = threadIdx.x;
+  const float qsc = p.q_scale[t];
+  const float *grow = p.grad + t * p.ld_grad;
+  for (int i = tid; i < H * D; i += kBT) {
+    const uint32_t byte = p.q_fp8[t * H * (int64_t)D + i];
+    qd[i] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(byte, 1.0f, false)[0] * qsc;
+  }
+  // key list: dense, positions 0..pos; sparse, the valid entries in slot order
+  int n;
+  if (kDense) {
+    n = (int)(row_pos(s, t) + 1);
+  } else {
+    if (tid == 0) {
+      int c = 0;
+      for (int i = 0; i < k; ++i) {
+        const int v = p.idx[t * k + i];
+        if (v >= 0 && v < s.kvlen) rows[c++] = i;   // the slot; its position is idx[slot]
+      }
+      nvalid = c;
+    }
+    __syncthreads();
+    n = nvalid;
+  }
+  float dqa[kSBMaxQ];
+#pragma unroll
+  for (int i = 0; i < kSBMaxQ; ++i) dqa[i] = 0.f;
+  float dwa = 0.f;
+  for (int c0 = 0; c0 < n; c0 += kSBKeys) {
+    __syncthreads();
+    if (tid < kSBKeys) {
+      const int c = c0 + tid;
+      int pos = 0;
+      float g = 0.f;
+      if (c < n) {
+        const int slot = kDense ? c : rows[c];
+        pos = kDense ? c : p.idx[t * k + slot];
+        g = grow[slot];
+      }
+      pc[tid] = pos;
+      gc[tid] = g;
+    }
+    __syncthreads();
+    for (int i = tid; i < kSBKeys * D; i += kBT) {
+      const int c = i / D, d = i % D;
+      const uint32_t byte = p.k_fp8[(s.kv0 + pc[c]) * (int64_t)D + d];
+      kc[c][d] = c0 + c < n ? __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(byte, 1.0f, false)[0] *
+                                  p.k_scale[s.kv0 + pc[c]]
+                            : 0.f;
+    }
+    __syncthreads();
+    for (int i = tid; i < H * kSBKeys; i += kBT) {
+      const int j = i / kSBKeys, c = i % kSBKeys;
+      float z = 0.f;
+      for (int d = 0; d < D; ++d) z = fmaf(qd[j * D + d], kc[c][d], z);
+      ec[j][c] = z > 0.f ? gc[c] * p.w[t * H + j] : 0.f;
+      rc[j][c] = gc[c] * fmaxf(z, 0.f);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kSBMaxQ; ++q) {
+      const int i = tid + kBT * q;
+      if (i < H * D) {
+        const int j = i / D, d = i % D;
+        float a = dqa[q];
+        for (int c = 0; c < kSBKeys; ++c) a = fmaf(ec[j][c], kc[c][d], a);
+        dqa[q] = a;
+      }
+    }
+    for (int i = tid; i < kSBKeys * D; i += kBT) {
+      const int c = i / D, d = i % D;
+      if (c0 + c >= n) continue;
+      float a = 0.f;
+      for (int j = 0; j < H; ++j) a = fmaf(ec[j][c], qd[j * D + d], a);
+      unsafeAtomicAdd(p.dk + (s.kv0 + pc[c]) * (int64_t)D + d, a);
+    }
+    if (tid < H)
+      for (int c = 0; c < kSBKeys; ++c) dwa += rc[tid][c];
+  }
+#pragma unroll
+  for (int q = 0; q < kSBMaxQ; ++q) {
+    const int i = tid + kBT * q;
+    if (i < H * D) p.dq[t * H * (int64_t)D + i] = dqa[q];
+  }
+  if (tid < H) p.dw[t * H + tid] = dwa;
+}
+
+}  // namespace
+
+hipError_t launch_indexer_backward(const IndexerBwdArgs &a, hipStream_t stream) {
+  if (a.seq.total_q == 0) return hipSuccess;
+  const dim3 grid((unsigned)a.seq.total_q), block(kBT);
+  const bool dense = a.idx == nullptr;
+  if (a.idx_heads == 64 && a.idx_dim == 128) {
+    if (dense) hipLaunchKernelGGL(indexer_bwd_kernel<true>, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(indexer_bwd_kernel<false>, grid, block, 0, stream, a);
+  } else {
+    if (dense) hipLaunchKernelGGL(small_indexer_bwd_kernel<true>, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(small_indexer_bwd_kernel<false>, grid, block, 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -83,7 +83,27 @@ struct AlignArgs {
   float scale;
 };
 
+// Indexer backward: grad rows are ld_grad apart (sparse: by entry of idx;
+// dense, idx == nullptr: by key position); dq and dw are written, dk is
+// added to.
+struct IndexerBwdArgs {
+  SeqLayout seq;
+  const uint8_t *q_fp8;
+  const float *q_scale;
+  const float *w;
+  const uint8_t *k_fp8;
+  const float *k_scale;
+  const int32_t *idx;
+  const float *grad;
+  int64_t ld_grad;
+  float *dq;
+  float *dw;
+  float *dk;
+  int32_t idx_heads, idx_dim, k;
+};
+
 hipError_t launch_indexer(const IndexerArgs &a, hipStream_t stream);
+hipError_t launch_indexer_backward(const IndexerBwdArgs &a, hipStream_t stream);
 hipError_t launch_align_loss(const AlignArgs &a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs &a, hipStream_t stream);
 hipError_t launch_sparse_attn(const AttnArgs &a, hipStream_t stream);

@@ -7,6 +7,14 @@ Tolerances (fixed for this path):
 * top-k: bit-identical to the oracle selector run on the GPU's own scores;
 * attention (given identical indices): max-abs <= 2e-2 and relative
   Frobenius error <= 1e-2.
+* indexer backward (given identical indices and gradient): each element of
+  dq, dw and dk within 2^-12 of the sum of its terms' magnitudes, plus, for
+  (head, key) pairs whose dot product lies within 2^-16 of the sum of its
+  products' magnitudes from 0, that pair's whole term (the ReLU mask there
+  may fall either way: the GPU sums the 128 exact e4m3 products in fp32,
+  with error up to 2^-17 of that sum).  The GPU splits the gradient into two
+  bf16 terms (2^-17 relative) and accumulates in fp32 over at most a few
+  hundred MFMA steps, far inside 2^-12.
 * alignment loss (given identical scores, indices and the GPU attention's
   lse): gradient max-abs <= 1e-4 * max_s (p_s + q_s) of the row, and
   |loss - oracle| <= 1e-4 * max(1, sum_s p_s (|ln p_s| + |ln q_s|)).  The GPU
@@ -164,3 +172,55 @@ def check_align_rows(loss, grad, q, kv, scores, rows, kv0s, kvlens, positions, s
         worst_g = max(worst_g, gerr / pq)
         worst_l = max(worst_l, lerr / bound)
     return worst_g, worst_l
+
+
+BWD_REL = 2.0 ** -12
+BWD_AMBIG = 2.0 ** -16
+
+
+def indexer_backward_reference(inp, rows, positions, kv0s, grads, idx=None):
+    """Float64 oracle dq, dw for the given packed rows and their dk
+    contributions, with error bounds (see the tolerance note above).
+
+    grads[i] is row i's gradient (aligned with idx[i] when idx is given,
+    else by position).  Returns (dq, dq_bound, dw, dw_bound, dk_dict,
+    dk_bound_dict) with dk keyed by packed key row."""
+    dq_l, dqb_l, dw_l, dwb_l = [], [], [], []
+    dk, dkb = {}, {}
+    for i, r in enumerate(rows):
+        qd = oracle.dequantize(inp["q_fp8"][r:r + 1].cpu().numpy(), inp["q_scale"][r:r + 1].cpu().numpy())[0]
+        w = inp["w"][r].cpu().double().numpy()
+        g_row = np.asarray(grads[i], dtype=np.float64)
+        if idx is None:
+            keys = np.arange(int(positions[i]) + 1)
+            g = g_row[: keys.size]
+        else:
+            sel = np.asarray(idx[i])
+            ok = sel >= 0
+            keys, g = sel[ok].astype(np.int64), g_row[: sel.size][ok]
+        krow = kv0s[i] + keys
+        kd = oracle.dequantize(inp["k_fp8"][torch.as_tensor(krow)].cpu().numpy(),
+                               inp["k_scale"][torch.as_tensor(krow)].cpu().numpy())
+        dqr, dwr, dkr = oracle.indexer_backward_row(qd, w, kd, g)
+        z = qd @ kd.T
+        amb = np.abs(z) <= BWD_AMBIG * (np.abs(qd) @ np.abs(kd).T)
+        gw = np.abs(w)[:, None] * np.abs(g)[None, :]
+        e_abs = (z > 0) * gw
+        dq_l.append(dqr)
+        dqb_l.append(BWD_REL * (e_abs @ np.abs(kd)) + (amb * gw) @ np.abs(kd))
+        dw_l.append(dwr)
+        dwb_l.append(BWD_REL * (np.abs(z) * (z > 0)) @ np.abs(g) + 1e-30)
+        kb = BWD_REL * (e_abs.T @ np.abs(qd)) + (amb * gw).T @ np.abs(qd)
+        for n, kr in enumerate(krow):
+            dk[kr] = dk.get(kr, 0.0) + dkr[n]
+            dkb[kr] = dkb.get(kr, 0.0) + kb[n]
+    return np.stack(dq_l), np.stack(dqb_l), np.stack(dw_l), np.stack(dwb_l), dk, dkb
+
+
+def check_within(got, ref, bound, what):
+    err = np.abs(np.asarray(got, dtype=np.float64) - ref)
+    bad = ~(err <= bound + 1e-30)
+    assert not bad.any(), (f"{what}: {int(bad.sum())} of {bad.size} outside the bound; worst "
+                           f"err {err[bad].max():.3e} vs bound {np.asarray(bound)[bad].max():.3e}")
+    return float((err / (bound + 1e-30)).max())
+

@@ -229,3 +229,28 @@ def test_align_loss_shares_the_attention_shape_checks():
     assert _align(_problem(max_kv_len=3728271, total_kv=3728271), ld=3728272,
                   idx=None, ld_grad=3728272) == binding.DSA_ERR_UNSUPPORTED
     assert "max_kv_len" in _msg()
+
+
+def _ibwd(p, idx=FAKE, grad=FAKE, dq=FAKE, dw=FAKE, dk=FAKE, ld_grad=2048):
+    lib = binding.load_library()
+    return lib.dsa_indexer_backward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, idx, grad, ld_grad,
+                                    dq, dw, dk, None)
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(grad=None), binding.DSA_ERR_INVALID_ARGUMENT, "grad"),
+    (dict(dq=FAKE + 4), binding.DSA_ERR_INVALID_ARGUMENT, "dq"),
+    (dict(dw=None), binding.DSA_ERR_INVALID_ARGUMENT, "dw"),
+    (dict(dk=None), binding.DSA_ERR_INVALID_ARGUMENT, "dk"),
+    (dict(idx=FAKE + 8), binding.DSA_ERR_INVALID_ARGUMENT, "topk_idx"),
+    (dict(ld_grad=100), binding.DSA_ERR_INVALID_ARGUMENT, "ld_grad"),
+    (dict(idx=None, ld_grad=4000), binding.DSA_ERR_INVALID_ARGUMENT, "max_kv_len"),
+])
+def test_indexer_backward_rejects_bad_arguments(kw, status, needle):
+    assert _ibwd(_problem(), **kw) == status
+    assert needle in _msg()
+
+
+def test_indexer_backward_shares_the_indexer_shape_checks():
+    assert _ibwd(_problem(idx_dim=48)) == binding.DSA_ERR_UNSUPPORTED
+    assert _ibwd(_problem(idx_heads=0)) == binding.DSA_ERR_INVALID_ARGUMENT

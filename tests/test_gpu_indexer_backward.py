@@ -1,0 +1,206 @@
+"""GPU parity of the indexer backward (dsa_indexer_backward) against the
+float64 oracle.
+
+The score gradient is either seeded synthetic values or the alignment loss's
+own gradient; indices come from the library's top-k on seeded inputs, or are
+built in the test.  dq and dw are compared row by row, dk (accumulated by
+atomics over every row) key by key, within the bounds in tests/gpu_helpers.py.
+Covered: the MFMA path (H_I = 64, d_I = 128) in both forms with ragged last
+tiles, -1 entries anywhere and an empty row; two chunk calls adding into one
+dk; the fp32 path for other shapes; and sampled rows of the last chunk of the
+128K prefill (with the gradient zero outside the sampled rows, so that dk is
+known exactly)."""
+import numpy as np
+import pytest
+import torch
+
+from sparse_attention_18_amd import binding as dsa
+from sparse_attention_18_amd import workloads as wk
+from tests import gpu_helpers as H
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+MED = wk.PREFILL_4K.scaled(seq_len=700, topk=256, heads=128)
+
+
+def _announce(name):
+    print(f"[gpu-case] {name}", flush=True)
+
+
+def _topk(prob, g):
+    scores = H.run_indexer(prob, g)
+    idx = torch.empty(prob.total_q, prob.c.topk, dtype=torch.int32, device=DEV)
+    n = dsa.workspace_bytes(prob, dsa.WS_TOPK)
+    dsa.topk(prob, scores, idx, workspace=torch.empty(n, dtype=torch.uint8, device=DEV) if n else None)
+    torch.cuda.synchronize()
+    return scores, idx
+
+
+def _backward(prob, g, grad, idx, dk=None):
+    c = prob.c
+    dq = torch.full((c.total_q, c.idx_heads, c.idx_dim), float("nan"), dtype=torch.float32, device=DEV)
+    dw = torch.full((c.total_q, c.idx_heads), float("nan"), dtype=torch.float32, device=DEV)
+    if dk is None:
+        dk = torch.zeros(c.total_kv, c.idx_dim, dtype=torch.float32, device=DEV)
+    dsa.indexer_backward(prob, g["q_fp8"], g["q_scale"], g["w"], g["k_fp8"], g["k_scale"], grad, dq, dw,
+                         dk, idx=idx)
+    torch.cuda.synchronize()
+    return dq, dw, dk
+
+
+def _check(inp, prob, rows, positions, kv0s, grad, idx, dq, dw, dk, all_rows=True):
+    gr = grad.cpu().double().numpy()
+    ix = idx.cpu().numpy() if idx is not None else None
+    ref = H.indexer_backward_reference(inp, rows, positions, kv0s, [gr[r] for r in rows],
+                                       None if ix is None else [ix[r] for r in rows])
+    dq_r, dq_b, dw_r, dw_b, dk_r, dk_b = ref
+    H.check_within(dq[rows].cpu().numpy(), dq_r, dq_b, "dq")
+    H.check_within(dw[rows].cpu().numpy(), dw_r, dw_b, "dw")
+    if all_rows:
+        dkg = dk.cpu().double().numpy()
+        keys = sorted(dk_r)
+        H.check_within(dkg[keys], np.stack([dk_r[x] for x in keys]), np.stack([dk_b[x] for x in keys]), "dk")
+        untouched = np.ones(dkg.shape[0], dtype=bool)
+        untouched[keys] = False
+        assert not dkg[untouched].any(), "dk rows no row selected must stay zero"
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_backward_sparse_mfma(seed):
+    wl = MED
+    _announce(f"indexer backward sparse L={wl.seq_len} k={wl.topk} seed={seed}")
+    inp = wk.generate(wl)
+    prob = dsa.Problem.from_workload(wl, inp)
+    g = H.to_dev(inp)
+    _, idx = _topk(prob, g)
+    gen = torch.Generator(device="cpu").manual_seed(100 + seed)
+    grad = (torch.randn(prob.total_q, wl.topk, generator=gen) * 1e-3).to(DEV)
+    grad[idx < 0] = float("nan")        # entries past the selection are never read
+    dq, dw, dk = _backward(prob, g, grad, idx)
+    L = wl.seq_len
+    _check(inp, prob, list(range(L)), list(range(L)), [0] * L, torch.nan_to_num(grad), idx, dq, dw, dk)
+
+
+def test_backward_dense_mfma():
+    wl = MED.scaled(seq_len=300)
+    _announce("indexer backward dense L=300")
+    inp = wk.generate(wl)
+    prob = dsa.Problem.from_workload(wl, inp)
+    g = H.to_dev(inp)
+    ld = prob.ld_scores()
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    grad = torch.randn(prob.total_q, ld, generator=gen) * 1e-3
+    for r in range(300):
+        grad[r, r + 1:] = float("nan")   # past pos: never read
+    dq, dw, dk = _backward(prob, g, grad.to(DEV), None)
+    L = wl.seq_len
+    _check(inp, prob, list(range(L)), list(range(L)), [0] * L, torch.nan_to_num(grad), None, dq, dw, dk)
+
+
+def test_backward_custom_indices_gaps_and_empty_row():
+    wl = MED.scaled(seq_len=400, topk=80)
+    _announce("indexer backward sparse, -1 anywhere, empty row")
+    inp = wk.generate(wl)
+    prob = dsa.Problem.from_workload(wl, inp)
+    g = H.to_dev(inp)
+    L, k = wl.seq_len, wl.topk
+    rng = np.random.default_rng(11)
+    idx_np = np.full((L, k), -1, dtype=np.int32)
+    for r in range(L):
+        m = min(r + 1, int(rng.integers(1, k + 1)))
+        idx_np[r, rng.choice(k, size=m, replace=False)] = rng.choice(r + 1, size=m, replace=False)
+    idx_np[5] = -1
+    idx = torch.as_tensor(idx_np, device=DEV)
+    grad = torch.as_tensor(rng.standard_normal((L, k)) * 1e-3, dtype=torch.float32, device=DEV)
+    dq, dw, dk = _backward(prob, g, grad, idx)
+    _check(inp, prob, list(range(L)), list(range(L)), [0] * L, grad, idx, dq, dw, dk)
+    assert not dq[5].any() and not dw[5].any()
+
+
+def test_backward_chunks_add_into_one_dk():
+    """Two chunk calls (rows [0, 300) and [300, 600)) adding into one dk give
+    the single call's dk."""
+    wl = MED.scaled(seq_len=600)
+    _announce("indexer backward, two chunks into one dk")
+    inp = wk.generate(wl)
+    g = H.to_dev(inp)
+    prob = dsa.Problem.from_workload(wl, inp)
+    _, idx = _topk(prob, g)
+    gen = torch.Generator(device="cpu").manual_seed(3)
+    grad = (torch.randn(600, wl.topk, generator=gen) * 1e-3).to(DEV)
+    dq, dw, dk_all = _backward(prob, g, grad, idx)
+    dk = torch.zeros_like(dk_all)
+    for r0, r1 in ((0, 300), (300, 600)):
+        sub = {key: (v[r0:r1] if key in ("q_fp8", "q_scale", "w", "q") else v) for key, v in g.items()}
+        pc = dsa.Problem.from_workload(wl, inp, q_rows=slice(r0, r1), q_pos0=r0)
+        sub["k_fp8"], sub["k_scale"] = g["k_fp8"][:r1], g["k_scale"][:r1]
+        _backward(pc, sub, grad[r0:r1].contiguous(), idx[r0:r1].contiguous(), dk=dk[:r1])
+    # both dk are checked against the oracle over every row
+    _check(inp, prob, list(range(600)), list(range(600)), [0] * 600, grad, idx, dq, dw, dk)
+    _check(inp, prob, list(range(600)), list(range(600)), [0] * 600, grad, idx, dq, dw, dk_all)
+
+
+@pytest.mark.parametrize("wl", [wk.TINY_PREFILL, MED.scaled(seq_len=200, idx_heads=48, idx_dim=64, topk=64)],
+                         ids=["tiny_HI4_d32", "HI48_d64"])
+def test_backward_fp32_path(wl):
+    _announce(f"indexer backward fp32 path H_I={wl.idx_heads} d_I={wl.idx_dim}")
+    inp = wk.generate(wl)
+    prob = dsa.Problem.from_workload(wl, inp)
+    g = H.to_dev(inp)
+    _, idx = _topk(prob, g)
+    L = wl.seq_len
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    grad = (torch.randn(L, wl.topk, generator=gen) * 1e-3).to(DEV)
+    dq, dw, dk = _backward(prob, g, grad, idx)
+    _check(inp, prob, list(range(L)), list(range(L)), [0] * L, grad, idx, dq, dw, dk)
+    ld = prob.ld_scores()
+    gd = (torch.randn(L, ld, generator=gen) * 1e-3).to(DEV)
+    dq, dw, dk = _backward(prob, g, gd, None)
+    _check(inp, prob, list(range(L)), list(range(L)), [0] * L, gd, None, dq, dw, dk)
+
+
+def test_backward_of_the_alignment_loss_gradient():
+    """The composed training step: the alignment loss's gradient on the
+    scores carried back through the indexer."""
+    wl = MED.scaled(seq_len=500)
+    _announce("indexer backward of the alignment loss gradient")
+    inp = wk.generate(wl)
+    prob = dsa.Problem.from_workload(wl, inp)
+    g = H.to_dev(inp)
+    scores, idx = _topk(prob, g)
+    c = prob.c
+    out = torch.empty(c.total_q, c.heads, c.d_latent, dtype=torch.bfloat16, device=DEV)
+    lse = torch.empty(c.total_q, c.heads, dtype=torch.float32, device=DEV)
+    dsa.sparse_attn(prob, g["q"], g["kv"], idx, out, lse)
+    loss = torch.empty(c.total_q, dtype=torch.float32, device=DEV)
+    grad = torch.empty(c.total_q, c.topk, dtype=torch.float32, device=DEV)
+    dsa.indexer_align_loss(prob, g["q"], g["kv"], lse, scores, loss, grad, idx=idx)
+    dq, dw, dk = _backward(prob, g, grad, idx)
+    L = wl.seq_len
+    _check(inp, prob, list(range(L)), list(range(L)), [0] * L, grad, idx, dq, dw, dk)
+
+
+def test_backward_last_chunk_of_128k_prefill():
+    """The launch a training step makes per chunk, at full size: the last
+    4096-row chunk against the 131072-key prefix.  The gradient is nonzero on
+    a few sampled rows only, so dk is exactly their contribution."""
+    wl = wk.CHUNKED_PREFILL_128K
+    _announce("indexer backward 128K prefill, last chunk")
+    inp = wk.generate(wl, device=DEV)
+    L, C = wl.seq_len, wl.chunk
+    r0 = L - C
+    sl = slice(r0, L)
+    prob = dsa.Problem.from_workload(wl, inp, device=DEV, q_rows=sl, q_pos0=r0)
+    sub = dict(inp)
+    for key in ("q_fp8", "q_scale", "w", "q"):
+        sub[key] = inp[key][sl]
+    _, idx = _topk(prob, sub)
+    rows = [0, 1, 2047, 4095] + [int(x) for x in np.random.default_rng(9).integers(0, C, 4)]
+    rows = sorted(set(rows))
+    gen = torch.Generator(device="cpu").manual_seed(9)
+    grad = torch.zeros(C, wl.topk)
+    grad[rows] = torch.randn(len(rows), wl.topk, generator=gen) * 1e-3
+    grad = grad.to(DEV)
+    dq, dw, dk = _backward(prob, sub, grad, idx)
+    assert torch.isfinite(dq).all() and torch.isfinite(dw).all()
+    _check(sub, prob, rows, [r0 + r for r in rows], [0] * len(rows), grad, idx, dq, dw, dk)
