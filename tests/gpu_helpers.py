@@ -12,7 +12,8 @@ Tolerances (fixed for this path):
   (head, key) pairs whose dot product lies within 2^-16 of the sum of its
   products' magnitudes from 0, that pair's whole term (the ReLU mask there
   may fall either way: the GPU sums the 128 exact e4m3 products in fp32,
-  with error up to 2^-17 of that sum).  The GPU splits the gradient into two
+  with error up to 2^-17 of that sum); dw's terms g * ReLU(z) also carry
+  that dot-product error, so its bound adds 2^-16 of sum_s |g| * sum |q k|.  The GPU splits the gradient into two
   bf16 terms (2^-17 relative) and accumulates in fp32 over at most a few
   hundred MFMA steps, far inside 2^-12.
 * alignment loss (given identical scores, indices and the GPU attention's
@@ -209,7 +210,10 @@ def indexer_backward_reference(inp, rows, positions, kv0s, grads, idx=None):
         dq_l.append(dqr)
         dqb_l.append(BWD_REL * (e_abs @ np.abs(kd)) + (amb * gw) @ np.abs(kd))
         dw_l.append(dwr)
-        dwb_l.append(BWD_REL * (np.abs(z) * (z > 0)) @ np.abs(g) + 1e-30)
+        # the fp32 dot product errs by up to 2^-17 of the sum of its products'
+        # magnitudes, which ReLU passes on where z > 0
+        dwb_l.append(BWD_REL * (np.abs(z) * (z > 0)) @ np.abs(g)
+                     + BWD_AMBIG * (np.abs(qd) @ np.abs(kd).T) @ np.abs(g) + 1e-30)
         kb = BWD_REL * (e_abs.T @ np.abs(qd)) + (amb * gw).T @ np.abs(qd)
         for n, kr in enumerate(krow):
             dk[kr] = dk.get(kr, 0.0) + dkr[n]
