@@ -86,12 +86,12 @@ __device__ __forceinline__ v8bf lds_v8bf(const DSA_LDS uint8_t *p) {
 template <bool kDense>
 __global__ __launch_bounds__(kBT) void indexer_bwd_kernel(IndexerBwdArgs p) {
   constexpr int H = 64, D = 128;
-  __shared__ __attribute__((aligned(16))) uint8_t ktile[2][kBKeys * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t ktile[3][kBKeys * 128];
   __shared__ __attribute__((aligned(16))) uint8_t kT[D * 128];          // bf16 [dims][64]
   __shared__ __attribute__((aligned(16))) uint8_t eh[2][H * 128];       // bf16 [heads][keys]: hi, lo
   __shared__ __attribute__((aligned(16))) uint8_t et[2][kBKeys * 128];  // bf16 [keys][heads]: hi, lo
-  __shared__ float tks[2][kBKeys], tg[2][kBKeys];
-  __shared__ int tpos[2][kBKeys];
+  __shared__ float tks[3][kBKeys], tg[3][kBKeys];
+  __shared__ int tpos[3][kBKeys];
   __shared__ int idxl[kDense ? 1 : kBMaxK];
   __shared__ uint16_t slotl[kDense ? 1 : kBMaxK];
   __shared__ int s_scan[4];
@@ -162,12 +162,18 @@ __global__ __launch_bounds__(kBT) void indexer_bwd_kernel(IndexerBwdArgs p) {
 
   // Tile staging: each thread carries two 16-byte chunks of the 64 key rows;
   // threads 0..63 also the key's scale, gradient and position.  Keys past m
-  // get zero bytes and a zero gradient.
+  // get zero bytes and a zero gradient (their loads read key m - 1, so every
+  // load is issued unconditionally).  Two register sets take turns: the
+  // loads for tile i + 2 go out at the start of tile i, into the set tile i
+  // came from, and reach LDS at the end of tile i + 1 -- two tiles of work
+  // in between, since a gathered row takes longer than one tile to arrive.
   const uint8_t *kseq = p.k_fp8 + s.kv0 * D;
-  v4i st[2];
-  float st_ks = 0.f, st_g = 0.f;
-  int st_pos = 0;
-  auto fetch = [&](int t0) {
+  struct Stage {
+    v4i k[2];
+    float ks, g;
+    int pos;
+  };
+  auto fetch = [&](Stage &st, int t0) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int chunk = tid + kBT * e, n = chunk >> 3, j = chunk & 7;
@@ -175,27 +181,25 @@ __global__ __launch_bounds__(kBT) void indexer_bwd_kernel(IndexerBwdArgs p) {
       const int cc = c < m ? c : m - 1;
       const int pos = kDense ? cc : idxl[cc];
       const v4i x = *reinterpret_cast<const v4i *>(kseq + (int64_t)pos * D + 16 * j);
-      st[e] = c < m ? x : v4i{0, 0, 0, 0};
+      st.k[e] = c < m ? x : v4i{0, 0, 0, 0};
     }
-    if (tid < kBKeys) {
-      const int c = t0 + tid;
-      const int cc = c < m ? c : m - 1;
-      st_pos = kDense ? cc : idxl[cc];
-      st_ks = p.k_scale[s.kv0 + st_pos];
-      const float gv = grow[kDense ? cc : (int)slotl[cc]];
-      st_g = c < m ? gv : 0.f;
-    }
+    const int c = t0 + (tid & (kBKeys - 1));
+    const int cc = c < m ? c : m - 1;
+    st.pos = kDense ? cc : idxl[cc];
+    st.ks = p.k_scale[s.kv0 + st.pos];
+    const float gv = grow[kDense ? cc : (int)slotl[cc]];
+    st.g = c < m ? gv : 0.f;
   };
-  auto commit = [&](int buf) {
+  auto commit = [&](const Stage &st, int buf) {
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int chunk = tid + kBT * e, n = chunk >> 3, j = chunk & 7;
-      *reinterpret_cast<v4i *>(&ktile[buf][f8_off(n, j)]) = st[e];
+      *reinterpret_cast<v4i *>(&ktile[buf][f8_off(n, j)]) = st.k[e];
     }
     if (tid < kBKeys) {
-      tks[buf][tid] = st_ks;
-      tg[buf][tid] = st_g;
-      tpos[buf][tid] = st_pos;
+      tks[buf][tid] = st.ks;
+      tg[buf][tid] = st.g;
+      tpos[buf][tid] = st.pos;
     }
   };
 
@@ -208,20 +212,22 @@ __global__ __launch_bounds__(kBT) void indexer_bwd_kernel(IndexerBwdArgs p) {
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) dq[nb] = v4f{0.f, 0.f, 0.f, 0.f};
 
+  Stage sa, sb;
   if (m > 0) {
-    // Q8 transposed to bf16 [dims][heads] (through ktile[1] and kT), then
+    fetch(sa, 0);
+    fetch(sb, kBKeys);
+    // Q8 transposed to bf16 [dims][heads] (through ktile[2] and kT), then
     // read once as the dk products' B operands: dim nb*16 + r16, heads
     // 32*ks + 8*g4 .. +7.
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int chunk = tid + kBT * e, n = chunk >> 3, j = chunk & 7;
-      *reinterpret_cast<v4i *>(&ktile[1][f8_off(n, j)]) =
+      *reinterpret_cast<v4i *>(&ktile[2][f8_off(n, j)]) =
           *reinterpret_cast<const v4i *>(p.q_fp8 + (t * H + n) * (int64_t)D + 16 * j);
     }
-    fetch(0);
-    commit(0);
+    commit(sa, 0);
     __syncthreads();
-    transpose_f8_bf16((const DSA_LDS uint8_t *)ktile[1], (DSA_LDS uint8_t *)kT, tid);
+    transpose_f8_bf16((const DSA_LDS uint8_t *)ktile[2], (DSA_LDS uint8_t *)kT, tid);
     __syncthreads();
   }
   v8bf qb[8][2];
@@ -235,10 +241,10 @@ __global__ __launch_bounds__(kBT) void indexer_bwd_kernel(IndexerBwdArgs p) {
 
   const int key_l = 16 * wave + r16;   // this lane's tile key in the z layout
   float *dkseq = p.dk + s.kv0 * D;
-  int buf = 0;
-  for (int t0 = 0; t0 < m; t0 += kBKeys) {
-    const bool has_next = t0 + kBKeys < m;
-    if (has_next) fetch(t0 + kBKeys);
+  // One tile: loads for tile + 2 into `ld`, compute from LDS buffer `buf`,
+  // then `cm` (tile + 1's data) into the next buffer.
+  auto tile_step = [&](int t0, int buf, Stage &ld, const Stage &cm) {
+    fetch(ld, t0 + 2 * kBKeys);
     const DSA_LDS uint8_t *kt = (const DSA_LDS uint8_t *)ktile[buf];
     // z for keys 16*wave + r16 (B: that key's dims 32*g4 .. +31), all heads.
     v4f z[4];
@@ -303,17 +309,24 @@ __global__ __launch_bounds__(kBT) void indexer_bwd_kernel(IndexerBwdArgs p) {
     // element j: key 16*wave + 4*g4 + j, dim nb*16 + r16
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      // keys past m have E = 0: they add zeros to key m - 1's row, which
+      // keeps the atomics (vector-memory ops) out of a branch
       const int key = 16 * wave + 4 * g4 + j;
-      if (t0 + key < m) {
-        const float f = qsc / tks[buf][key];
-        float *drow = dkseq + (int64_t)tpos[buf][key] * D + r16;
+      const float f = qsc / tks[buf][key];
+      float *drow = dkseq + (int64_t)tpos[buf][key] * D + r16;
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) unsafeAtomicAdd(drow + nb * 16, dkb[nb][j] * f);
-      }
+      for (int nb = 0; nb < 8; ++nb) unsafeAtomicAdd(drow + nb * 16, dkb[nb][j] * f);
     }
-    if (has_next) commit(buf ^ 1);
+    commit(cm, buf == 2 ? 0 : buf + 1);
     __syncthreads();
-    buf ^= 1;
+  };
+  for (int t0 = 0, buf = 0; t0 < m; t0 += 2 * kBKeys) {
+    tile_step(t0, buf, sa, sb);
+    buf = buf == 2 ? 0 : buf + 1;
+    if (t0 + kBKeys < m) {
+      tile_step(t0 + kBKeys, buf, sb, sa);
+      buf = buf == 2 ? 0 : buf + 1;
+    }
   }
 
   // dw: sum over the 16 lanes of a row group (keys), then over the waves.
