@@ -43,10 +43,11 @@ constexpr int kBMaxK = 4096;
 __device__ __forceinline__ int f8_off(int n, int j) { return n * 128 + 16 * (j ^ ((n >> 1) & 7)); }
 
 // Byte offset of bf16 element c of row r in an array of 64-element (128-byte)
-// rows; the 16-byte chunks of row r are XOR-swizzled by r & 7, so 16 lanes
-// reading the same chunk of 16 consecutive rows spread over the banks.
+// rows; the 16-byte chunks of row r are XOR-swizzled by (r ^ (r >> 3)) & 7,
+// so 16 lanes reading the same chunk of 16 consecutive rows, and the
+// transpose writing rows 8 apart, spread over the banks.
 __device__ __forceinline__ int b16_off(int r, int c) {
-  return r * 128 + ((((c >> 3) ^ r) & 7) << 4) + (c & 7) * 2;
+  return r * 128 + ((((c >> 3) ^ r ^ (r >> 3)) & 7) << 4) + (c & 7) * 2;
 }
 
 // bf16 bits of a float that is exactly representable (an e4m3 value).
@@ -265,8 +266,11 @@ __global__ __launch_bounds__(kBT) void indexer_bwd_kernel(IndexerBwdArgs p) {
         const float zr = z[hb][j];
         dw[hb][j] = fmaf(fmaxf(zr, 0.f), cw, dw[hb][j]);
         const float e = zr > 0.f ? wv[hb][j] * gk : 0.f;
-        hiw[j] = f32_to_bf16_bits(e);
-        low[j] = f32_to_bf16_bits(e - bf16_bits_to_f32(hiw[j]));
+        // hi = e rounded to bf16 (round to nearest even), lo = the remainder
+        const __bf16 eh16 = (__bf16)e;
+        const __bf16 el16 = (__bf16)(e - (float)eh16);
+        hiw[j] = __builtin_bit_cast(uint16_t, eh16);
+        low[j] = __builtin_bit_cast(uint16_t, el16);
         const int head = hb * 16 + 4 * g4 + j;
         *reinterpret_cast<uint16_t *>(&eh[0][b16_off(head, key_l)]) = (uint16_t)hiw[j];
         *reinterpret_cast<uint16_t *>(&eh[1][b16_off(head, key_l)]) = (uint16_t)low[j];
