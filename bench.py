@@ -10,7 +10,8 @@ sequences, cached contexts uniform in [8K, 128K]) and reports it as
 ``decode_us_per_step``, and the same decode step over paged caches (64-row
 blocks, shuffled) as ``decode_paged_us_per_step``.  ``train_align`` times the
 sparse-stage training step: the same 32 chunks, each followed by the indexer
-alignment loss over its selected keys (loss and score gradient per row).
+alignment loss over its selected keys (loss and score gradient per row) and
+the indexer backward (that gradient carried to dq, dw and dk).
 
 Per-stage durations come from HIP events recorded around each stage call on
 the stream the kernels run on.  ``roofline`` covers the dominant stage:
@@ -55,7 +56,8 @@ def log(msg):
 _KERNEL_SOURCES = {"sparse_attn": ["sparse_attn.hip", "kv_gather.h", "common.h", "launch.h"],
                    "indexer": ["indexer.hip", "common.h", "launch.h"],
                    "topk": ["topk.hip", "common.h", "launch.h"],
-                   "align_loss": ["align.hip", "kv_gather.h", "common.h", "launch.h"]}
+                   "align_loss": ["align.hip", "kv_gather.h", "common.h", "launch.h"],
+                   "indexer_bwd": ["indexer_bwd.hip", "common.h", "launch.h"]}
 
 
 def measured_traffic(stage: str):
@@ -112,6 +114,21 @@ def align_bytes(wl, positions):
     return float(m.sum()) * (wl.d_qk * 2 + 12) + per_tok * len(m)
 
 
+def indexer_bwd_bytes(wl, positions):
+    """Indexer backward, read or written once: per selected pair the key row,
+    its scale and the score gradient (128 + 4 + 4 B); per query q8, w, q_scale
+    in and dq (fp32), dw out; dk (fp32) once per key."""
+    m = np.minimum(np.asarray(positions, dtype=np.float64) + 1, wl.topk)
+    per_tok = wl.idx_heads * wl.idx_dim * (1 + 4) + wl.idx_heads * 4 * 2 + 4
+    return float(m.sum()) * (wl.idx_dim + 8) + per_tok * len(m) + 4.0 * wl.idx_dim * len(m)
+
+
+def indexer_bwd_flops(wl, positions):
+    """z (2 H_I d_I), dq and dk (2 H_I d_I each) per selected pair."""
+    m = np.minimum(np.asarray(positions, dtype=np.float64) + 1, wl.topk)
+    return float(m.sum()) * 6.0 * wl.idx_heads * wl.idx_dim
+
+
 def align_flops(wl, positions):
     m = np.minimum(np.asarray(positions, dtype=np.float64) + 1, wl.topk)
     return float(m.sum()) * 2.0 * wl.heads * wl.d_qk
@@ -163,8 +180,13 @@ class ChunkedPrefill:
         its selected keys (while the chunk's scores are still in place)."""
         inp, wl = self.inp, self.wl
         if not hasattr(self, "grad"):
-            self.grad = torch.empty(wl.chunk, wl.topk, dtype=torch.float32, device=self.scores.device)
-            self.loss = torch.empty(wl.seq_len, dtype=torch.float32, device=self.scores.device)
+            dev = self.scores.device
+            self.grad = torch.empty(wl.chunk, wl.topk, dtype=torch.float32, device=dev)
+            self.loss = torch.empty(wl.seq_len, dtype=torch.float32, device=dev)
+            self.dq = torch.empty(wl.chunk, wl.idx_heads, wl.idx_dim, dtype=torch.float32, device=dev)
+            self.dw = torch.empty(wl.chunk, wl.idx_heads, dtype=torch.float32, device=dev)
+            self.dk = torch.zeros(wl.seq_len, wl.idx_dim, dtype=torch.float32, device=dev)
+        self.dk.zero_()
         for ci, (r0, sl, prob) in enumerate(self.chunks):
             rows = sl.stop - sl.start
             scores = self.scores[:rows]
@@ -180,6 +202,11 @@ class ChunkedPrefill:
                                    self.loss[sl], self.grad[:rows], idx=self.idx[sl], ld=self.ld)
             if events is not None:
                 events[ci][1].record()
+            dsa.indexer_backward(prob, inp["q_fp8"][sl], inp["q_scale"][sl], inp["w"][sl],
+                                 inp["k_fp8"][: sl.stop], inp["k_scale"][: sl.stop], self.grad[:rows],
+                                 self.dq[:rows], self.dw[:rows], self.dk[: sl.stop], idx=self.idx[sl])
+            if events is not None:
+                events[ci][2].record()
 
 
 def run_prefill(args, dev):
@@ -253,7 +280,7 @@ def run_train(bench, steps=2):
     bench.train_step()
     torch.cuda.synchronize()
     nch = len(bench.chunks)
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(nch)]
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nch)]
            for _ in range(steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
@@ -263,10 +290,20 @@ def run_train(bench, steps=2):
     torch.cuda.synchronize()
     step_ms = start.elapsed_time(end) / steps
     loss_ms = sum(e[0].elapsed_time(e[1]) for st in evs for e in st) / steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for st in evs for e in st) / steps
     pos = bench.positions
     t = loss_ms * 1e-3
     rate = align_bytes(wl, pos) / t
-    log(f"[bench] training step {step_ms:.1f} ms, alignment loss {loss_ms:.2f} ms")
+    tb = bwd_ms * 1e-3
+    brate = indexer_bwd_bytes(wl, pos) / tb
+    log(f"[bench] training step {step_ms:.1f} ms, alignment loss {loss_ms:.2f} ms, "
+        f"indexer backward {bwd_ms:.2f} ms")
+    bwd = {"ms_per_step": round(bwd_ms, 3), "launches_per_step": nch,
+           "avg_launch_us": round(bwd_ms / nch * 1e3, 1), "bound": "hbm",
+           "achieved": round(brate / 1e9, 1), "peak": round(HBM_PEAK / 1e9, 1), "unit": "GB/s",
+           "frac": round(brate / HBM_PEAK, 4),
+           "tflops": round(indexer_bwd_flops(wl, pos) / tb / 1e12, 1),
+           "traffic": measured_traffic("indexer_bwd")}
     return {"ms_per_step": round(loss_ms, 3), "launches_per_step": nch,
             "avg_launch_us": round(loss_ms / nch * 1e3, 1), "bound": "hbm",
             "achieved": round(rate / 1e9, 1), "peak": round(HBM_PEAK / 1e9, 1), "unit": "GB/s",
@@ -275,6 +312,7 @@ def run_train(bench, steps=2):
             "traffic": measured_traffic("align_loss"),
             "train_step_ms": round(step_ms, 3),
             "train_tokens_per_s": round(wl.seq_len / (step_ms * 1e-3), 1),
+            "indexer_backward": bwd,
             "steps": steps}
 
 
