@@ -316,6 +316,55 @@ def run_train(bench, steps=2):
             "steps": steps}
 
 
+def train_cpu_baseline(bench, wl, rows_n=512, batch=32):
+    """The float64 oracle's alignment loss and indexer backward on sampled rows
+    of the last chunk, on the GPU's own scores, indices and score gradient.
+    Rows are copied to the host a batch at a time (untimed); only the oracle
+    calls are timed."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    inp, L, C = bench.inp, wl.seq_len, wl.chunk
+    r0 = L - C
+    rows_all = np.linspace(0, C - 1, rows_n).astype(np.int64)
+    dt = 0.0
+    for b0 in range(0, rows_n, batch):
+        rows = rows_all[b0:b0 + batch]
+        idx = bench.idx[r0 + rows].cpu().numpy()
+        sc = bench.scores[rows].cpu().double().numpy()      # the last chunk's scores
+        g = bench.grad[rows].cpu().double().numpy()
+        cases = []
+        for i, r in enumerate(rows):
+            keys = idx[i][idx[i] >= 0].astype(np.int64)
+            at = torch.as_tensor(keys)
+            cases.append(dict(
+                q=inp["q"][r0 + r].cpu().double().numpy(), kv=inp["kv"][at].cpu().double().numpy(),
+                qd=oracle.dequantize(inp["q_fp8"][r0 + r:r0 + r + 1].cpu().numpy(),
+                                     inp["q_scale"][r0 + r:r0 + r + 1].cpu().numpy())[0],
+                w=inp["w"][r0 + r].cpu().double().numpy(),
+                kd=oracle.dequantize(inp["k_fp8"][at].cpu().numpy(), inp["k_scale"][at].cpu().numpy()),
+                s=sc[i][keys], g=g[i][: keys.size], pos=r0 + int(r), m=keys.size))
+        t0 = time.perf_counter()
+        for c in cases:
+            local = np.arange(c["m"])[None]
+            oracle.alignment_loss_rows(c["q"][None], c["kv"], [c["s"]], [c["pos"]], wl.softmax_scale,
+                                       idx=local)
+            oracle.indexer_backward_rows(c["qd"][None], c["w"][None], c["kd"], [c["pos"]], [c["g"]],
+                                         idx=local)
+        dt += time.perf_counter() - t0
+    log(f"[bench] training cpu baseline: {dt:.1f}s for {rows_n} rows")
+    return {"value": round(rows_n / dt, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{rows_n} rows of the last 4096-row chunk, 2048 selected keys each "
+                      f"(alignment loss and indexer backward in float64 per row, on the GPU's "
+                      f"scores, indices and score gradient; every row of the step costs the same "
+                      f"except the first 2048, so the rate stands for the whole step)",
+            "seconds": round(dt, 2)}
+
+
 def run_decode(args, dev):
     wl = wk.DECODE_B64
     t0 = time.time()
@@ -446,6 +495,8 @@ def main():
     train = None
     if not args.no_train:
         train = run_train(bench)
+        if not args.no_cpu_baseline:
+            train["cpu_baseline"] = train_cpu_baseline(bench, wl)
     decode_us = decode_paged_us = None
     if not args.no_decode:
         decode_us, decode_paged_us, _ = run_decode(args, dev)
