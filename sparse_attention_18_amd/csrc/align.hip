@@ -254,9 +254,19 @@ __global__ __launch_bounds__(NW * 64) void align_loss_kernel(AlignArgs p) {
         if (g2) gb = gather_setup(tt + 2, vo);
         const DSA_LDS uint8_t *tb = (const DSA_LDS uint8_t *)kvbuf[tt % kAStages];
         v16f s0 = {}, s1 = {};
+        // B operands read LA k-steps ahead: the scheduling barrier below keeps
+        // each step's instructions in place, so a read issued right before its
+        // MFMA would expose the LDS latency at every step
+        constexpr int LA = 4;
+        v4i bq[LA];
+#pragma unroll
+        for (int kk = 0; kk < LA; ++kk)
+          bq[kk] = *reinterpret_cast<const DSA_LDS v4i *>(tb + tile_off(c32, 2 * kk + G));
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
-          const v4i b = *reinterpret_cast<const DSA_LDS v4i *>(tb + tile_off(c32, 2 * kk + G));
+          const v4i b = bq[kk % LA];
+          if (kk + LA < KS)
+            bq[kk % LA] = *reinterpret_cast<const DSA_LDS v4i *>(tb + tile_off(c32, 2 * (kk + LA) + G));
           if (kk & 1) s1 = mfma_32x32x16_bf16(qa[kk], as_v8bf(b), s1);
           else s0 = mfma_32x32x16_bf16(qa[kk], as_v8bf(b), s0);
           if (g2)
