@@ -446,11 +446,13 @@ dsa_status align_impl(const dsa_problem *p, const uint16_t *q, const uint16_t *k
   DSA_TRY(check_ptr(loss, hq, "loss"));
   DSA_TRY(check_ptr(grad, hq, "grad"));
   if (topk_idx != nullptr) DSA_TRY(check_ptr(topk_idx, hq, "topk_idx"));
+  // With no query rows nothing is read or written (an empty index array may
+  // reach here as NULL, which would otherwise select the dense form's bound).
   const int64_t need = topk_idx != nullptr ? (int64_t)p->topk : p->max_kv_len;
-  DSA_CHECK(ld_grad >= need && ld_grad >= 1, DSA_ERR_INVALID_ARGUMENT,
+  DSA_CHECK(!hq || (ld_grad >= need && ld_grad >= 1), DSA_ERR_INVALID_ARGUMENT,
             "ld_grad (%lld) must be >= %s (%lld) and >= 1", (long long)ld_grad,
             topk_idx != nullptr ? "topk" : "max_kv_len", (long long)need);
-  DSA_CHECK(p->total_q == 0 || ld_grad <= INT64_MAX / 4 / p->total_q, DSA_ERR_INVALID_ARGUMENT,
+  DSA_CHECK(!hq || ld_grad <= INT64_MAX / 4 / p->total_q, DSA_ERR_INVALID_ARGUMENT,
             "grad matrix size overflows");
   dsa::AlignArgs a;
   a.seq = layout_of(p);
@@ -500,11 +502,13 @@ dsa_status indexer_bwd_impl(const dsa_problem *p, const uint8_t *q_fp8, const fl
   DSA_TRY(check_ptr(dw, hq, "dw"));
   DSA_TRY(check_ptr(dk, p->total_kv > 0, "dk"));
   if (topk_idx != nullptr) DSA_TRY(check_ptr(topk_idx, hq, "topk_idx"));
+  // With no query rows nothing is read or written (an empty index array may
+  // reach here as NULL, which would otherwise select the dense form's bound).
   const int64_t need = topk_idx != nullptr ? (int64_t)p->topk : p->max_kv_len;
-  DSA_CHECK(ld_grad >= need && ld_grad >= 1, DSA_ERR_INVALID_ARGUMENT,
+  DSA_CHECK(!hq || (ld_grad >= need && ld_grad >= 1), DSA_ERR_INVALID_ARGUMENT,
             "ld_grad (%lld) must be >= %s (%lld) and >= 1", (long long)ld_grad,
             topk_idx != nullptr ? "topk" : "max_kv_len", (long long)need);
-  DSA_CHECK(p->total_q == 0 || ld_grad <= INT64_MAX / 4 / p->total_q, DSA_ERR_INVALID_ARGUMENT,
+  DSA_CHECK(!hq || ld_grad <= INT64_MAX / 4 / p->total_q, DSA_ERR_INVALID_ARGUMENT,
             "grad matrix size overflows");
   DSA_CHECK(p->max_kv_len <= INT32_MAX, DSA_ERR_UNSUPPORTED, "max_kv_len must fit int32");
   dsa::IndexerBwdArgs a;
