@@ -77,7 +77,7 @@ typedef struct dsa_problem {
 } dsa_problem;
 
 /* Workspace selectors for dsa_workspace_bytes(). */
-enum { DSA_WS_TOPK = 0, DSA_WS_ATTN = 1, DSA_WS_FORWARD = 2 };
+enum { DSA_WS_TOPK = 0, DSA_WS_ATTN = 1, DSA_WS_FORWARD = 2, DSA_WS_INDEXER_BWD = 3 };
 
 /*
  * Stage 1, lightning indexer (r.nikiv.dev summary, "How DSA Works"; the
@@ -264,16 +264,28 @@ dsa_status dsa_indexer_align_loss(const dsa_problem *p, const uint16_t *q, const
  * The (H_I, d_I) = (64, 128) shape runs on MFMA: the mask is decided on the
  * fp32 dot product of the exact e4m3 values and the products use bf16
  * operands with the gradient split into two bf16 terms (about 2^-17
- * relative), fp32 accumulation.  Other shapes take a plain fp32 path.  dk
- * must be ordinary device memory (hipMalloc): fp32 atomics add to it.
+ * relative), fp32 accumulation.  Other shapes take a plain fp32 path.
+ *   workspace / workspace_bytes: optional.  NULL: dk is added to with fp32
+ *         atomics (dk must then be ordinary device memory, hipMalloc).  In
+ *         the sparse form on the (64, 128) shape a workspace of at least
+ *         dsa_workspace_bytes(p, DSA_WS_INDEXER_BWD) bytes (16-byte aligned;
+ *         about total_q * k * 516 bytes) selects the faster two-pass form:
+ *         each (row, key) contribution is stored there and a second kernel
+ *         sums them per block of 64 keys and adds the sums to dk (no atomics
+ *         to memory).  Its contents need no initialisation and are
+ *         overwritten.  Other forms ignore it.  Too small: DSA_ERR_WORKSPACE.
+ * Calls that overlap on one stream's timeline and add into the same dk rows
+ * must be ordered by the caller (the two-pass form reads and writes dk).
  */
 dsa_status dsa_indexer_backward(const dsa_problem *p, const uint8_t *q_fp8, const float *q_scale,
                                 const float *w, const uint8_t *k_fp8, const float *k_scale,
                                 const int32_t *topk_idx, const float *grad, int64_t ld_grad,
-                                float *dq, float *dw, float *dk, void *stream);
+                                float *dq, float *dw, float *dk, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /* Bytes of device workspace the given entry point needs for problem p
- * (which = DSA_WS_TOPK, DSA_WS_ATTN or DSA_WS_FORWARD); 0 if none.  Returns
+ * (which = DSA_WS_TOPK, DSA_WS_ATTN, DSA_WS_FORWARD, or DSA_WS_INDEXER_BWD
+ * for the two-pass form of dsa_indexer_backward); 0 if none.  Returns
  * (size_t)-1 for an invalid problem (see dsa_last_error).  The paged entry
  * points need the same amounts. */
 size_t dsa_workspace_bytes(const dsa_problem *p, int which);

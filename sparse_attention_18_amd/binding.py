@@ -23,7 +23,7 @@ DSA_ERR_INVALID_ARGUMENT = 1
 DSA_ERR_UNSUPPORTED = 2
 DSA_ERR_WORKSPACE = 3
 DSA_ERR_HIP = 4
-WS_TOPK, WS_ATTN, WS_FORWARD = 0, 1, 2
+WS_TOPK, WS_ATTN, WS_FORWARD, WS_INDEXER_BWD = 0, 1, 2, 3
 
 EXPORTED = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward",
             "dsa_indexer_scores_paged", "dsa_sparse_attn_paged", "dsa_forward_paged",
@@ -103,7 +103,7 @@ def load_library():
         lib.dsa_sparse_attn_paged.argtypes = [P, G, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.dsa_forward_paged.argtypes = [P, G, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.dsa_indexer_align_loss.argtypes = [P, vp, vp, vp, vp, i64, vp, vp, vp, i64, vp]
-        lib.dsa_indexer_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp]
+        lib.dsa_indexer_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]
         for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward",
                      "dsa_indexer_scores_paged", "dsa_sparse_attn_paged", "dsa_forward_paged",
                      "dsa_indexer_align_loss", "dsa_indexer_backward"):
@@ -304,12 +304,14 @@ def indexer_align_loss(prob: Problem, q, kv, lse, scores, loss, grad, idx=None, 
 
 
 def indexer_backward(prob: Problem, q_fp8, q_scale, w, k_fp8, k_scale, grad, dq, dw, dk, idx=None,
-                     stream=None):
+                     workspace=None, stream=None):
     """dsa_indexer_backward: the score gradient ``grad`` carried to dq [total_q, H_I,
     d_I], dw [total_q, H_I] (both overwritten) and dk [total_kv, d_I] (added to).
 
     Sparse form (``idx`` given): grad is aligned with idx; dense form (``idx``
-    None): grad is by position, grad.shape[1] >= max_kv_len."""
+    None): grad is by position, grad.shape[1] >= max_kv_len.  ``workspace`` (a
+    uint8 tensor of at least ``workspace_bytes(prob, WS_INDEXER_BWD)`` bytes)
+    selects the two-pass dk of the sparse form; None: dk by atomics."""
     c = prob.c
     if not isinstance(grad, torch.Tensor) or grad.dim() != 2:
         raise ValueError("grad must be a 2-D tensor")
@@ -325,7 +327,9 @@ def indexer_backward(prob: Problem, q_fp8, q_scale, w, k_fp8, k_scale, grad, dq,
         _ptr(grad, torch.float32, "grad", (c.total_q, ld_grad)), ld_grad,
         _ptr(dq, torch.float32, "dq", (c.total_q, c.idx_heads, c.idx_dim)),
         _ptr(dw, torch.float32, "dw", (c.total_q, c.idx_heads)),
-        _ptr(dk, torch.float32, "dk", (c.total_kv, c.idx_dim)), _stream(stream)))
+        _ptr(dk, torch.float32, "dk", (c.total_kv, c.idx_dim)),
+        _ptr(workspace, torch.uint8, "workspace") if workspace is not None else None,
+        workspace.numel() if workspace is not None else 0, _stream(stream)))
 
 
 class PagedKV:

@@ -249,6 +249,14 @@ size_t ws_attn(const dsa_problem *p) {
 size_t ws_topk(const dsa_problem *p, int64_t ld) {
   return dsa::topk_workspace_bytes(topk_args(p, nullptr, ld, nullptr));
 }
+size_t ws_indexer_bwd(const dsa_problem *p) {
+  dsa::IndexerBwdArgs a{};
+  a.seq = layout_of(p);
+  a.idx_heads = p->idx_heads;
+  a.idx_dim = p->idx_dim;
+  a.k = p->topk;
+  return dsa::indexer_bwd_workspace_bytes(a);
+}
 
 // Layout of dsa_forward's workspace: scores | indices | top-k scratch | attention scratch.
 struct ForwardWs {
@@ -279,6 +287,7 @@ size_t dsa_workspace_bytes(const dsa_problem *p, int which) {
     case DSA_WS_TOPK: return ws_topk(p, forward_ld(p));
     case DSA_WS_ATTN: return ws_attn(p);
     case DSA_WS_FORWARD: return forward_ws(p).total;
+    case DSA_WS_INDEXER_BWD: return ws_indexer_bwd(p);
     default: fail(DSA_ERR_INVALID_ARGUMENT, "unknown workspace selector %d", which); return (size_t)-1;
   }
 }
@@ -492,7 +501,8 @@ namespace {
 dsa_status indexer_bwd_impl(const dsa_problem *p, const uint8_t *q_fp8, const float *q_scale,
                             const float *w, const uint8_t *k_fp8, const float *k_scale,
                             const int32_t *topk_idx, const float *grad, int64_t ld_grad, float *dq,
-                            float *dw, float *dk, void *stream) {
+                            float *dw, float *dk, void *workspace, size_t workspace_bytes,
+                            void *stream) {
   DSA_TRY(check_problem(p));
   DSA_TRY(check_indexer_dims(p));
   DSA_TRY(check_indexer_ptrs(p, q_fp8, q_scale, w, k_fp8, k_scale));
@@ -511,7 +521,14 @@ dsa_status indexer_bwd_impl(const dsa_problem *p, const uint8_t *q_fp8, const fl
   DSA_CHECK(!hq || ld_grad <= INT64_MAX / 4 / p->total_q, DSA_ERR_INVALID_ARGUMENT,
             "grad matrix size overflows");
   DSA_CHECK(p->max_kv_len <= INT32_MAX, DSA_ERR_UNSUPPORTED, "max_kv_len must fit int32");
-  dsa::IndexerBwdArgs a;
+  if (workspace != nullptr && topk_idx != nullptr) {
+    const size_t need = ws_indexer_bwd(p);
+    DSA_CHECK(workspace_bytes >= need, DSA_ERR_WORKSPACE,
+              "indexer backward workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+    DSA_CHECK(aligned16(workspace), DSA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+    DSA_CHECK(p->total_kv / 64 < INT32_MAX, DSA_ERR_UNSUPPORTED, "total_kv too large for the workspace path");
+  }
+  dsa::IndexerBwdArgs a{};
   a.seq = layout_of(p);
   a.q_fp8 = q_fp8;
   a.q_scale = q_scale;
@@ -527,6 +544,9 @@ dsa_status indexer_bwd_impl(const dsa_problem *p, const uint8_t *q_fp8, const fl
   a.idx_heads = p->idx_heads;
   a.idx_dim = p->idx_dim;
   a.k = p->topk;
+  // the dense form and the fp32 path take no workspace
+  a.workspace = topk_idx != nullptr ? workspace : nullptr;
+  a.workspace_bytes = workspace_bytes;
   return hip_status(dsa::launch_indexer_backward(a, static_cast<hipStream_t>(stream)),
                     "indexer backward launch");
 }
@@ -538,9 +558,10 @@ extern "C" {
 dsa_status dsa_indexer_backward(const dsa_problem *p, const uint8_t *q_fp8, const float *q_scale,
                                 const float *w, const uint8_t *k_fp8, const float *k_scale,
                                 const int32_t *topk_idx, const float *grad, int64_t ld_grad,
-                                float *dq, float *dw, float *dk, void *stream) {
+                                float *dq, float *dw, float *dk, void *workspace,
+                                size_t workspace_bytes, void *stream) {
   return indexer_bwd_impl(p, q_fp8, q_scale, w, k_fp8, k_scale, topk_idx, grad, ld_grad, dq, dw,
-                          dk, stream);
+                          dk, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

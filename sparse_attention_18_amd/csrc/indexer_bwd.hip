@@ -12,22 +12,31 @@
 //     dq~[t, j]  = sum_s E[j, s] * k8[s],      E[j, s] = g[t, s] * w[t, j] * k_scale[s] * [z > 0]
 //     dk~[s]    += (q_scale[t] / k_scale[s]) * sum_j E[j, s] * q8[t, j]
 //
-// MFMA path (H_I = 64, d_I = 128): one workgroup of 4 waves per token; keys
-// in 64-key tiles, double-buffered in LDS as in the prefill indexer.
-//  * z on v_mfma_f32_16x16x128_f8f6f4 straight from the FP8 bytes (wave w:
-//    keys 16w..16w+15, all 64 heads), so the ReLU mask is decided on the
-//    fp32 dot product of the exact e4m3 values.
+// MFMA path (H_I = 64, d_I = 128): one workgroup of 8 waves per token; keys
+// in 64-key tiles, staged through LDS in three buffers.
+//  * z on v_mfma_f32_16x16x128_f8f6f4 straight from the FP8 bytes, so the
+//    ReLU mask is decided on the fp32 dot product of the exact e4m3 values.
 //  * E is formed in fp32 and split into two bf16 terms (hi + lo carries it to
 //    about 2^-17); e4m3 values are exact in bf16.  dq~ = E . K8 and the
 //    tile's dk~ block = E^T . Q8 run on v_mfma_f32_16x16x32_bf16 (a hi and a
-//    lo product each) with fp32 accumulation: wave w owns heads 16w.. of dq
-//    (all 128 dims, in registers across the tiles) and keys 16w.. of each
-//    tile's dk block.
+//    lo product each) with fp32 accumulation; dq stays in registers across
+//    the tiles.
 //  * dq contracts over keys and dk over heads, so E goes to LDS twice
 //    (head-major and key-major), each key tile is transposed once into bf16
 //    (dims x keys), and Q8's transpose is built once per token.
 //  * A key is selected by many queries, so dk rows of different tokens
-//    collide: each tile's block is added to dk with fp32 atomics.
+//    collide.  Without a workspace each tile's block is added to dk with
+//    fp32 atomics; these are resolved beyond the L2 (about one 4-byte write
+//    to HBM per atomic), which makes them the kernel's bound.  With one
+//    (sparse form), dk is formed in two passes with no atomics to memory:
+//    the token kernel stores each (token, key) contribution, 128 floats, at
+//    the key's rank in the token's ascending key list, along with that list
+//    and, per 64-key block of the sequence, where the block's keys start in
+//    it; then one workgroup per 64-key block gathers the contributions to
+//    its keys from every token of the sequence, adds them in LDS and adds
+//    the sums to dk once.
+#include <climits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -84,8 +93,50 @@ __device__ __forceinline__ v8bf lds_v8bf(const DSA_LDS uint8_t *p) {
   return __builtin_bit_cast(v8bf, *reinterpret_cast<const DSA_LDS v4i *>(p));
 }
 
-template <bool kDense>
-__global__ __launch_bounds__(kBT) void indexer_bwd_kernel(IndexerBwdArgs p) {
+// Eight waves, two per SIMD: the dk atomics of a wave fill its in-order
+// vector-memory counter, so a wave that has issued them cannot wait for its
+// next key tile without waiting for them as well; with two waves per SIMD the
+// other one computes meanwhile.  Wave w: z and E for keys 16(w%4).. and head
+// blocks 2(w/4), 2(w/4)+1; dq for heads 16(w%4).. and dims 64(w/4)..; the dk
+// block for keys 16(w%4).. and dims 64(w/4)..
+constexpr int kBW = 8;              // waves per workgroup (MFMA path)
+constexpr int kBT8 = kBW * 64;
+
+constexpr int kRKB = 64;   // keys per block of the two-pass dk reduction
+
+// Ascending sort of the token's compacted (position, entry) pairs in LDS,
+// bitonic over the next power of two >= m (<= kBMaxK) with INT_MAX padding.
+// Called by every thread of the workgroup.
+__device__ void sort_keys(int *key, uint16_t *val, int m, int tid) {
+  int n2 = 1;
+  while (n2 < m) n2 <<= 1;
+  for (int i = m + tid; i < n2; i += kBT8) {
+    key[i] = INT_MAX;
+    val[i] = 0;
+  }
+  __syncthreads();
+  for (int size = 2; size <= n2; size <<= 1)
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < n2 / 2; i += kBT8) {
+        const int lo = 2 * i - (i & (stride - 1)), hi = lo + stride;
+        const bool up = (lo & size) == 0;
+        const int a = key[lo], b = key[hi];
+        if ((a > b) == up) {
+          key[lo] = b;
+          key[hi] = a;
+          const uint16_t t = val[lo];
+          val[lo] = val[hi];
+          val[hi] = t;
+        }
+      }
+      __syncthreads();
+    }
+}
+
+// kStore (sparse form only): the two-pass dk; see the file comment.
+template <bool kDense, bool kStore>
+__global__ __launch_bounds__(kBT8) void indexer_bwd_kernel(IndexerBwdArgs p) {
+  static_assert(!(kDense && kStore), "the stored contributions are for the sparse form");
   constexpr int H = 64, D = 128;
   __shared__ __attribute__((aligned(16))) uint8_t ktile[3][kBKeys * 128];
   __shared__ __attribute__((aligned(16))) uint8_t kT[D * 128];          // bf16 [dims][64]
@@ -95,12 +146,13 @@ __global__ __launch_bounds__(kBT) void indexer_bwd_kernel(IndexerBwdArgs p) {
   __shared__ int tpos[3][kBKeys];
   __shared__ int idxl[kDense ? 1 : kBMaxK];
   __shared__ uint16_t slotl[kDense ? 1 : kBMaxK];
-  __shared__ int s_scan[4];
+  __shared__ int s_scan[kBW];
   __shared__ float sdw[4][H];
 
   const int64_t t = __builtin_amdgcn_workgroup_id_x();
   const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w4 = wave & 3, wh = wave >> 2;   // key / head-or-dim quarter and half of this wave
   const int r16 = lane & 15, g4 = lane >> 4;
   const int k = p.k;
 
@@ -110,22 +162,24 @@ __global__ __launch_bounds__(kBT) void indexer_bwd_kernel(IndexerBwdArgs p) {
   const float qsc = p.q_scale[t];
   const float *grow = p.grad + t * p.ld_grad;
 
-  // z operands (A of 16x16x128): head hb*16 + r16, dims 32*g4 .. +31.
-  v8i qa[4];
-  float wv[4][4];   // w of this lane's result heads hb*16 + 4*g4 + j
+  // z operands (A of 16x16x128) for head blocks hb = 2*wh + i: head
+  // hb*16 + r16, dims 32*g4 .. +31; w of the lane's result heads hb*16 + 4*g4 + j.
+  v8i qa[2];
+  float wv[2][4];
 #pragma unroll
-  for (int hb = 0; hb < 4; ++hb) {
+  for (int i = 0; i < 2; ++i) {
+    const int hb = 2 * wh + i;
     const v4i *src = reinterpret_cast<const v4i *>(p.q_fp8 + (t * H + hb * 16 + r16) * (int64_t)D + 32 * g4);
     const v4i lo = src[0], hi = src[1];
-    qa[hb] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    qa[i] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) wv[hb][j] = p.w[t * H + hb * 16 + 4 * g4 + j];
+    for (int j = 0; j < 4; ++j) wv[i][j] = p.w[t * H + hb * 16 + 4 * g4 + j];
   }
 
   // Key set: m keys; sparse, compacted with their entry slots.
   int m;
   if constexpr (!kDense) {
-    constexpr int per = kBMaxK / kBT;
+    constexpr int per = kBMaxK / kBT8;
     const int32_t *irow = p.idx + t * k;
     const int i0 = tid * per;
     int vals[per];
@@ -144,7 +198,7 @@ __global__ __launch_bounds__(kBT) void indexer_bwd_kernel(IndexerBwdArgs p) {
     int base = inc - cnt;
     m = 0;
 #pragma unroll
-    for (int w2 = 0; w2 < 4; ++w2) {
+    for (int w2 = 0; w2 < kBW; ++w2) {
       const int x = s_scan[w2];
       base += w2 < wave ? x : 0;
       m += x;
@@ -157,11 +211,36 @@ __global__ __launch_bounds__(kBT) void indexer_bwd_kernel(IndexerBwdArgs p) {
         ++base;
       }
     __syncthreads();
+    if constexpr (kStore) {
+      // Contributions go to the key's rank in the ascending list: the
+      // top-k's lists already are; others are sorted here.
+      int unsorted = 0;
+      for (int c = tid; c + 1 < m; c += kBT8) unsorted |= idxl[c] > idxl[c + 1];
+      if (__syncthreads_or(unsorted)) sort_keys(idxl, slotl, m, tid);
+      int32_t *krow = p.skey + t * p.kpad;
+      for (int c = tid; c < m; c += kBT8) krow[c] = idxl[c];
+      // bnd[t][jl]: how many of the token's keys lie below the start of the
+      // sequence's 64-key block jl (blocks of packed key rows, counted from
+      // the one holding the sequence's first key), for jl = 0 .. nb.
+      const int64_t jlo = s.kv0 / kRKB;
+      const int nb = s.kvlen > 0 ? (int)((s.kv0 + s.kvlen - 1) / kRKB - jlo + 1) : 0;
+      int32_t *brow = p.bnd + t * p.nbr;
+      for (int jl = tid; jl <= nb; jl += kBT8) {
+        const int64_t thr = (jlo + jl) * kRKB - s.kv0;
+        int lo = 0, hi = m;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (idxl[mid] < thr) lo = mid + 1;
+          else hi = mid;
+        }
+        brow[jl] = lo;
+      }
+    }
   } else {
     m = row_ok ? (int)(row_pos(s, t) + 1) : 0;
   }
 
-  // Tile staging: each thread carries two 16-byte chunks of the 64 key rows;
+  // Tile staging: each thread carries one 16-byte chunk of the 64 key rows;
   // threads 0..63 also the key's scale, gradient and position.  Keys past m
   // get zero bytes and a zero gradient (their loads read key m - 1, so every
   // load is issued unconditionally).  Two register sets take turns: the
@@ -170,19 +249,18 @@ __global__ __launch_bounds__(kBT) void indexer_bwd_kernel(IndexerBwdArgs p) {
   // in between, since a gathered row takes longer than one tile to arrive.
   const uint8_t *kseq = p.k_fp8 + s.kv0 * D;
   struct Stage {
-    v4i k[2];
+    v4i k;
     float ks, g;
     int pos;
   };
   auto fetch = [&](Stage &st, int t0) {
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int chunk = tid + kBT * e, n = chunk >> 3, j = chunk & 7;
+    {
+      const int n = tid >> 3, j = tid & 7;
       const int c = t0 + n;
       const int cc = c < m ? c : m - 1;
       const int pos = kDense ? cc : idxl[cc];
       const v4i x = *reinterpret_cast<const v4i *>(kseq + (int64_t)pos * D + 16 * j);
-      st.k[e] = c < m ? x : v4i{0, 0, 0, 0};
+      st.k = c < m ? x : v4i{0, 0, 0, 0};
     }
     const int c = t0 + (tid & (kBKeys - 1));
     const int cc = c < m ? c : m - 1;
@@ -192,11 +270,7 @@ __global__ __launch_bounds__(kBT) void indexer_bwd_kernel(IndexerBwdArgs p) {
     st.g = c < m ? gv : 0.f;
   };
   auto commit = [&](const Stage &st, int buf) {
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int chunk = tid + kBT * e, n = chunk >> 3, j = chunk & 7;
-      *reinterpret_cast<v4i *>(&ktile[buf][f8_off(n, j)]) = st.k[e];
-    }
+    *reinterpret_cast<v4i *>(&ktile[buf][f8_off(tid >> 3, tid & 7)]) = st.k;
     if (tid < kBKeys) {
       tks[buf][tid] = st.ks;
       tg[buf][tid] = st.g;
@@ -204,68 +278,65 @@ __global__ __launch_bounds__(kBT) void indexer_bwd_kernel(IndexerBwdArgs p) {
     }
   };
 
-  float dw[4][4];
-  v4f dq[8];
+  float dw[2][4];
+  v4f dq[4];
 #pragma unroll
-  for (int hb = 0; hb < 4; ++hb)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dw[hb][j] = 0.f;
+    for (int j = 0; j < 4; ++j) dw[i][j] = 0.f;
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) dq[nb] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < 4; ++nb) dq[nb] = v4f{0.f, 0.f, 0.f, 0.f};
 
   Stage sa, sb;
   if (m > 0) {
     fetch(sa, 0);
     fetch(sb, kBKeys);
     // Q8 transposed to bf16 [dims][heads] (through ktile[2] and kT), then
-    // read once as the dk products' B operands: dim nb*16 + r16, heads
-    // 32*ks + 8*g4 .. +7.
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int chunk = tid + kBT * e, n = chunk >> 3, j = chunk & 7;
-      *reinterpret_cast<v4i *>(&ktile[2][f8_off(n, j)]) =
-          *reinterpret_cast<const v4i *>(p.q_fp8 + (t * H + n) * (int64_t)D + 16 * j);
-    }
+    // read once as the dk products' B operands: dim 64*wh + nb*16 + r16,
+    // heads 32*ks + 8*g4 .. +7.
+    *reinterpret_cast<v4i *>(&ktile[2][f8_off(tid >> 3, tid & 7)]) =
+        *reinterpret_cast<const v4i *>(p.q_fp8 + (t * H + (tid >> 3)) * (int64_t)D + 16 * (tid & 7));
     commit(sa, 0);
     __syncthreads();
-    transpose_f8_bf16((const DSA_LDS uint8_t *)ktile[2], (DSA_LDS uint8_t *)kT, tid);
+    if (tid < 256) transpose_f8_bf16((const DSA_LDS uint8_t *)ktile[2], (DSA_LDS uint8_t *)kT, tid);
     __syncthreads();
   }
-  v8bf qb[8][2];
+  v8bf qb[4][2];
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb)
+  for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
-      qb[nb][ks] = m > 0 ? lds_v8bf((const DSA_LDS uint8_t *)kT + b16_off(nb * 16 + r16, 32 * ks + 8 * g4))
+      qb[nb][ks] = m > 0 ? lds_v8bf((const DSA_LDS uint8_t *)kT + b16_off(64 * wh + nb * 16 + r16, 32 * ks + 8 * g4))
                          : v8bf{};
   __syncthreads();
 
-  const int key_l = 16 * wave + r16;   // this lane's tile key in the z layout
+  const int key_l = 16 * w4 + r16;   // this lane's tile key in the z layout
   float *dkseq = p.dk + s.kv0 * D;
   // One tile: loads for tile + 2 into `ld`, compute from LDS buffer `buf`,
   // then `cm` (tile + 1's data) into the next buffer.
   auto tile_step = [&](int t0, int buf, Stage &ld, const Stage &cm) {
     fetch(ld, t0 + 2 * kBKeys);
     const DSA_LDS uint8_t *kt = (const DSA_LDS uint8_t *)ktile[buf];
-    // z for keys 16*wave + r16 (B: that key's dims 32*g4 .. +31), all heads.
-    v4f z[4];
+    // z for key key_l (B: its dims 32*g4 .. +31) and the wave's two head blocks
+    v4f z[2];
     {
       const v4i lo = *reinterpret_cast<const DSA_LDS v4i *>(kt + f8_off(key_l, 2 * g4));
       const v4i hi = *reinterpret_cast<const DSA_LDS v4i *>(kt + f8_off(key_l, 2 * g4 + 1));
       const v8i bop = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-      for (int hb = 0; hb < 4; ++hb) z[hb] = mfma_16x16x128_fp8(qa[hb], bop, v4f{0.f, 0.f, 0.f, 0.f});
+      for (int i = 0; i < 2; ++i) z[i] = mfma_16x16x128_fp8(qa[i], bop, v4f{0.f, 0.f, 0.f, 0.f});
     }
     const float gk = tg[buf][key_l] * tks[buf][key_l];   // g * k_scale of the lane's key
     const float cw = gk * qsc;
 #pragma unroll
-    for (int hb = 0; hb < 4; ++hb) {
+    for (int i = 0; i < 2; ++i) {
+      const int hb = 2 * wh + i;
       uint32_t hiw[4], low[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float zr = z[hb][j];
-        dw[hb][j] = fmaf(fmaxf(zr, 0.f), cw, dw[hb][j]);
-        const float e = zr > 0.f ? wv[hb][j] * gk : 0.f;
+        const float zr = z[i][j];
+        dw[i][j] = fmaf(fmaxf(zr, 0.f), cw, dw[i][j]);
+        const float e = zr > 0.f ? wv[i][j] * gk : 0.f;
         // hi = e rounded to bf16 (round to nearest even), lo = the remainder
         const __bf16 eh16 = (__bf16)e;
         const __bf16 el16 = (__bf16)(e - (float)eh16);
@@ -281,45 +352,53 @@ __global__ __launch_bounds__(kBT) void indexer_bwd_kernel(IndexerBwdArgs p) {
       *reinterpret_cast<v2i *>(&et[1][b16_off(key_l, c0)]) =
           v2i{(int)(low[0] | (low[1] << 16)), (int)(low[2] | (low[3] << 16))};
     }
-    transpose_f8_bf16(kt, (DSA_LDS uint8_t *)kT, tid);
+    if (tid < 256) transpose_f8_bf16(kt, (DSA_LDS uint8_t *)kT, tid);
     __syncthreads();
 
-    // dq[heads 16*wave + ...][all dims] += E . K8   (K = the tile's keys)
+    // dq[heads 16*w4 + ...][dims 64*wh + ...] += E . K8   (K = the tile's keys)
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const v8bf ahi = lds_v8bf((const DSA_LDS uint8_t *)eh[0] + b16_off(16 * wave + r16, 32 * ks + 8 * g4));
-      const v8bf alo = lds_v8bf((const DSA_LDS uint8_t *)eh[1] + b16_off(16 * wave + r16, 32 * ks + 8 * g4));
+      const v8bf ahi = lds_v8bf((const DSA_LDS uint8_t *)eh[0] + b16_off(16 * w4 + r16, 32 * ks + 8 * g4));
+      const v8bf alo = lds_v8bf((const DSA_LDS uint8_t *)eh[1] + b16_off(16 * w4 + r16, 32 * ks + 8 * g4));
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const v8bf b = lds_v8bf((const DSA_LDS uint8_t *)kT + b16_off(nb * 16 + r16, 32 * ks + 8 * g4));
+      for (int nb = 0; nb < 4; ++nb) {
+        const v8bf b = lds_v8bf((const DSA_LDS uint8_t *)kT + b16_off(64 * wh + nb * 16 + r16, 32 * ks + 8 * g4));
         dq[nb] = mfma_16x16x32_bf16(ahi, b, dq[nb]);
         dq[nb] = mfma_16x16x32_bf16(alo, b, dq[nb]);
       }
     }
-    // dk block[keys 16*wave + ...][all dims] = E^T . Q8   (K = heads)
-    v4f dkb[8];
+    // dk block[keys 16*w4 + ...][dims 64*wh + ...] = E^T . Q8   (K = heads)
+    v4f dkb[4];
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) dkb[nb] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < 4; ++nb) dkb[nb] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const v8bf ahi = lds_v8bf((const DSA_LDS uint8_t *)et[0] + b16_off(16 * wave + r16, 32 * ks + 8 * g4));
-      const v8bf alo = lds_v8bf((const DSA_LDS uint8_t *)et[1] + b16_off(16 * wave + r16, 32 * ks + 8 * g4));
+      const v8bf ahi = lds_v8bf((const DSA_LDS uint8_t *)et[0] + b16_off(16 * w4 + r16, 32 * ks + 8 * g4));
+      const v8bf alo = lds_v8bf((const DSA_LDS uint8_t *)et[1] + b16_off(16 * w4 + r16, 32 * ks + 8 * g4));
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
+      for (int nb = 0; nb < 4; ++nb) {
         dkb[nb] = mfma_16x16x32_bf16(ahi, qb[nb][ks], dkb[nb]);
         dkb[nb] = mfma_16x16x32_bf16(alo, qb[nb][ks], dkb[nb]);
       }
     }
-    // element j: key 16*wave + 4*g4 + j, dim nb*16 + r16
+    // element j: key 16*w4 + 4*g4 + j, dim 64*wh + nb*16 + r16
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      // keys past m have E = 0: they add zeros to key m - 1's row, which
-      // keeps the atomics (vector-memory ops) out of a branch
-      const int key = 16 * wave + 4 * g4 + j;
+      const int key = 16 * w4 + 4 * g4 + j;
       const float f = qsc / tks[buf][key];
-      float *drow = dkseq + (int64_t)tpos[buf][key] * D + r16;
+      if constexpr (kStore) {
+        // the key's rank t0 + key < kpad (a multiple of 64 >= k); ranks past
+        // m get zeros, which the reduction never reads
+        float *crow = p.contrib + (t * p.kpad + t0 + key) * D + 64 * wh + r16;
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) unsafeAtomicAdd(drow + nb * 16, dkb[nb][j] * f);
+        for (int nb = 0; nb < 4; ++nb) __builtin_nontemporal_store(dkb[nb][j] * f, crow + nb * 16);
+      } else {
+        // keys past m have E = 0: they add zeros to key m - 1's row, which
+        // keeps the atomics (vector-memory ops) out of a branch
+        float *drow = dkseq + (int64_t)tpos[buf][key] * D + 64 * wh + r16;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) unsafeAtomicAdd(drow + nb * 16, dkb[nb][j] * f);
+      }
     }
     commit(cm, buf == 2 ? 0 : buf + 1);
     __syncthreads();
@@ -333,25 +412,195 @@ __global__ __launch_bounds__(kBT) void indexer_bwd_kernel(IndexerBwdArgs p) {
     }
   }
 
-  // dw: sum over the 16 lanes of a row group (keys), then over the waves.
+  // dw: sum over the 16 lanes of a row group (keys), then over the four waves
+  // that share the head blocks.
 #pragma unroll
-  for (int hb = 0; hb < 4; ++hb)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      float v = dw[hb][j];
+      float v = dw[i][j];
 #pragma unroll
       for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-      if (r16 == 0) sdw[wave][hb * 16 + 4 * g4 + j] = v;
+      if (r16 == 0) sdw[w4][(2 * wh + i) * 16 + 4 * g4 + j] = v;
     }
   __syncthreads();
   if (!row_ok) return;
   if (tid < H) p.dw[t * H + tid] = (sdw[0][tid] + sdw[1][tid]) + (sdw[2][tid] + sdw[3][tid]);
-  // dq: element j of block nb is head 16*wave + 4*g4 + j, dim nb*16 + r16
+  // dq: element j of block nb is head 16*w4 + 4*g4 + j, dim 64*wh + nb*16 + r16
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    float *qrow = p.dq + (t * H + 16 * wave + 4 * g4 + j) * (int64_t)D + r16;
+    float *qrow = p.dq + (t * H + 16 * w4 + 4 * g4 + j) * (int64_t)D + 64 * wh + r16;
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) qrow[nb * 16] = dq[nb][j];
+    for (int nb = 0; nb < 4; ++nb) qrow[nb * 16] = dq[nb][j];
+  }
+}
+
+// Second pass of the two-pass dk: one workgroup per block of 64 packed key
+// rows.  For every sequence whose keys overlap the block, its tokens are
+// taken 4096 at a time: each token's run of ranks [bnd[jl], bnd[jl + 1]) in
+// its ascending key list is exactly its keys in the block, so an exclusive
+// scan of the run lengths numbers the window's (token, key) pairs.  Pairs
+// are then handled kRCap at a time: every token writes its index over its
+// run (pair -> token), every pair's key is read once, and half-wave h, which
+// owns the block's keys 4h .. 4h+3, picks its pairs out by ballot and sums
+// their 128 floats in registers, kRU pairs in flight.  No two half-waves
+// touch one key, so nothing is atomic; at the end each adds its four rows to
+// dk.  Workgroup ids are laid out so that consecutive blocks run on one XCD
+// and share the bnd lines in its L2.
+constexpr int kRWin = 4096;            // tokens per scan window
+constexpr int kRCap = 8192;            // pairs per batch
+constexpr int kRT = 512;
+constexpr int kRHW = kRT / 32;         // half-waves, each owning kRKB / kRHW keys
+constexpr int kRChunk = 256;           // pair slots a half-wave scans at a time
+constexpr int kRU = 4;
+static_assert(kRKB == 4 * kRHW, "four keys per half-wave");
+
+__global__ __launch_bounds__(kRT) void dk_reduce_kernel(IndexerBwdArgs p, int nblk, int per) {
+  constexpr int D = 128;
+  __shared__ int s_lo[kRWin], s_ex[kRWin];
+  __shared__ uint16_t s_row[kRCap];
+  __shared__ uint8_t s_key[kRCap];
+  __shared__ uint16_t s_list[kRHW][kRChunk];
+  __shared__ int s_wsum[kRT / 64];
+  __shared__ int s_b0;
+  const int wid = __builtin_amdgcn_workgroup_id_x();
+  const int j = (wid & 7) * per + (wid >> 3);
+  if (j >= nblk) return;
+  const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hw = tid >> 5, l32 = tid & 31;
+  const int64_t G0 = (int64_t)j * kRKB;
+  const int64_t G1 = G0 + kRKB < p.seq.total_kv ? G0 + kRKB : p.seq.total_kv;
+  // this half-wave's sums: key 4*hw + kk, dims l32 + 32*q
+  float acc[4][4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[kk][q] = 0.f;
+  // first sequence whose keys end after G0 (key offsets are non-decreasing)
+  if (wave == 0) {
+    int cnt = 0;
+    for (int base = 0; base < p.seq.batch; base += 64) {
+      const int b = base + lane;
+      const bool le = b < p.seq.batch && (int64_t)p.seq.kv_offsets[b + 1] <= G0;
+      cnt += __popcll(__ballot(le));
+    }
+    if (lane == 0) s_b0 = cnt;
+  }
+  __syncthreads();
+  for (int b = s_b0; b < p.seq.batch; ++b) {
+    const SeqInfo s = load_seq(p.seq, b);
+    if (s.kv0 >= G1) break;
+    if (s.kvlen == 0 || s.kv0 + s.kvlen <= G0) continue;
+    const int jl = (int)(j - s.kv0 / kRKB);   // 0 <= jl < the sequence's block count
+    for (int64_t w0 = s.q0; w0 < s.q1; w0 += kRWin) {
+      const int nrow = (int)(s.q1 - w0 < kRWin ? s.q1 - w0 : kRWin);
+      // thread: tokens 8*tid .. +7 of the window; runs clamped into [0, kpad]
+      int lo8[8], len8[8], ex8[8], sum = 0;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = 8 * tid + e;
+        int lo = 0, hi = 0;
+        if (i < nrow) {
+          const int32_t *br = p.bnd + (w0 + i) * p.nbr + jl;
+          lo = br[0];
+          hi = br[1];
+          lo = lo < 0 ? 0 : (lo > p.kpad ? p.kpad : lo);
+          hi = hi < lo ? lo : (hi > p.kpad ? p.kpad : hi);
+        }
+        lo8[e] = lo;
+        len8[e] = hi - lo;
+        sum += hi - lo;
+      }
+      const int inc = (int)wave_scan<0>((uint32_t)sum);
+      if (lane == 63) s_wsum[wave] = inc;
+      __syncthreads();
+      int before = inc - sum, P = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < kRT / 64; ++w2) {
+        const int x = s_wsum[w2];
+        before += w2 < wave ? x : 0;
+        P += x;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = 8 * tid + e;
+        ex8[e] = before;
+        if (i < nrow) {
+          s_lo[i] = lo8[e];
+          s_ex[i] = before;
+        }
+        before += len8[e];
+      }
+      for (int P0 = 0; P0 < P; P0 += kRCap) {
+        const int np = P - P0 < kRCap ? P - P0 : kRCap;
+        // pair -> token over this batch
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int x0 = ex8[e] > P0 ? ex8[e] : P0;
+          const int x1 = ex8[e] + len8[e] < P0 + np ? ex8[e] + len8[e] : P0 + np;
+          for (int x = x0; x < x1; ++x) s_row[x - P0] = (uint16_t)(8 * tid + e);
+        }
+        __syncthreads();
+        // each pair's key, as an index into the block (255: not in it)
+#pragma unroll 4
+        for (int x = tid; x < np; x += kRT) {
+          const int i = s_row[x];
+          const int64_t e = (w0 + i) * p.kpad + s_lo[i] + (P0 + x - s_ex[i]);
+          const int64_t l = s.kv0 + p.skey[e] - G0;
+          s_key[x] = (l >= 0 && l < kRKB) ? (uint8_t)l : (uint8_t)255;
+        }
+        __syncthreads();
+        for (int base = 0; base < np; base += kRChunk) {
+          // this half-wave's pairs among slots base .. base + kRChunk - 1
+          int cnt = 0;
+#pragma unroll
+          for (int s2 = 0; s2 < kRChunk; s2 += 32) {
+            const int x = base + s2 + l32;
+            const int kk = x < np ? s_key[x] : 255;
+            const bool mine = (kk >> 2) == hw;
+            const uint32_t bits = (uint32_t)(__ballot(mine) >> (lane & 32));
+            if (mine) s_list[hw][cnt + __popc(bits & ((1u << l32) - 1))] = (uint16_t)x;
+            cnt += __popc(bits);
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          for (int q0 = 0; q0 < cnt; q0 += kRU) {
+            float v[kRU][4];
+            int kl[kRU];
+#pragma unroll
+            for (int u = 0; u < kRU; ++u) {
+              const int x = s_list[hw][q0 + u < cnt ? q0 + u : cnt - 1];
+              const int i = s_row[x];
+              const int64_t e = (w0 + i) * p.kpad + s_lo[i] + (P0 + x - s_ex[i]);
+              const float *src = p.contrib + e * D + l32;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) v[u][q] = __builtin_nontemporal_load(src + 32 * q);
+              kl[u] = q0 + u < cnt ? (s_key[x] & 3) : -1;
+            }
+#pragma unroll
+            for (int u = 0; u < kRU; ++u)
+#pragma unroll
+              for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[kk][q] += kl[u] == kk ? v[u][q] : 0.f;
+          }
+          __builtin_amdgcn_wave_barrier();   // s_list is rewritten by the next chunk
+        }
+        __syncthreads();   // s_row and s_key are rewritten by the next batch
+      }
+      __syncthreads();     // the next window rewrites s_lo, s_ex and s_wsum
+    }
+  }
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int64_t row = G0 + 4 * hw + kk;
+    if (row < G1) {
+      float *dst = p.dk + row * D + l32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) dst[32 * q] += acc[kk][q];
+    }
   }
 }
 
@@ -462,13 +711,61 @@ __global__ __launch_bounds__(kBT) void small_indexer_bwd_kernel(IndexerBwdArgs p
 
 }  // namespace
 
-hipError_t launch_indexer_backward(const IndexerBwdArgs &a, hipStream_t stream) {
-  if (a.seq.total_q == 0) return hipSuccess;
+namespace {
+
+// Two-pass workspace: contributions [total_q][kpad][128] f32 | ascending key
+// lists [total_q][kpad] i32 | block starts [total_q][nbr] i32.
+struct BwdWs {
+  size_t contrib, skey, bnd, total;
+  int32_t kpad, nbr;
+};
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+BwdWs bwd_ws(const IndexerBwdArgs &a) {
+  BwdWs w;
+  w.kpad = (a.k + kBKeys - 1) / kBKeys * kBKeys;
+  w.nbr = (int32_t)((a.seq.max_kv_len + kRKB - 1) / kRKB + 2);
+  const size_t rows = (size_t)a.seq.total_q;
+  w.contrib = round256(rows * (size_t)w.kpad * 128 * sizeof(float));
+  w.skey = round256(rows * (size_t)w.kpad * sizeof(int32_t));
+  w.bnd = round256(rows * (size_t)w.nbr * sizeof(int32_t));
+  w.total = w.contrib + w.skey + w.bnd;
+  return w;
+}
+
+}  // namespace
+
+size_t indexer_bwd_workspace_bytes(const IndexerBwdArgs &a) {
+  if (a.seq.total_q == 0 || a.idx_heads != 64 || a.idx_dim != 128) return 0;
+  return bwd_ws(a).total;
+}
+
+hipError_t launch_indexer_backward(const IndexerBwdArgs &a0, hipStream_t stream) {
+  if (a0.seq.total_q == 0) return hipSuccess;
+  IndexerBwdArgs a = a0;
   const dim3 grid((unsigned)a.seq.total_q), block(kBT);
   const bool dense = a.idx == nullptr;
   if (a.idx_heads == 64 && a.idx_dim == 128) {
-    if (dense) hipLaunchKernelGGL(indexer_bwd_kernel<true>, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(indexer_bwd_kernel<false>, grid, block, 0, stream, a);
+    if (dense) {
+      hipLaunchKernelGGL((indexer_bwd_kernel<true, false>), grid, dim3(kBT8), 0, stream, a);
+    } else if (a.workspace != nullptr) {
+      const BwdWs w = bwd_ws(a);
+      uint8_t *base = static_cast<uint8_t *>(a.workspace);
+      a.contrib = reinterpret_cast<float *>(base);
+      a.skey = reinterpret_cast<int32_t *>(base + w.contrib);
+      a.bnd = reinterpret_cast<int32_t *>(base + w.contrib + w.skey);
+      a.kpad = w.kpad;
+      a.nbr = w.nbr;
+      hipLaunchKernelGGL((indexer_bwd_kernel<false, true>), grid, dim3(kBT8), 0, stream, a);
+      if (a.seq.total_kv > 0) {
+        const int nblk = (int)((a.seq.total_kv + kRKB - 1) / kRKB);
+        const int per = (nblk + 7) / 8;
+        hipLaunchKernelGGL(dk_reduce_kernel, dim3(8 * (unsigned)per), dim3(kRT), 0, stream, a, nblk, per);
+      }
+    } else {
+      hipLaunchKernelGGL((indexer_bwd_kernel<false, false>), grid, dim3(kBT8), 0, stream, a);
+    }
   } else {
     if (dense) hipLaunchKernelGGL(small_indexer_bwd_kernel<true>, grid, block, 0, stream, a);
     else hipLaunchKernelGGL(small_indexer_bwd_kernel<false>, grid, block, 0, stream, a);

@@ -100,6 +100,15 @@ struct IndexerBwdArgs {
   float *dw;
   float *dk;
   int32_t idx_heads, idx_dim, k;
+  // Optional (nullptr: dk by atomics).  Sparse form on the MFMA shape: dk in
+  // two passes through at least indexer_bwd_workspace_bytes() bytes.
+  void *workspace;
+  size_t workspace_bytes;
+  // Set by the launcher from the workspace.
+  float *contrib;
+  int32_t *skey;
+  int32_t *bnd;
+  int32_t kpad, nbr;
 };
 
 hipError_t launch_indexer(const IndexerArgs &a, hipStream_t stream);
@@ -109,6 +118,7 @@ hipError_t launch_topk(const TopkArgs &a, hipStream_t stream);
 hipError_t launch_sparse_attn(const AttnArgs &a, hipStream_t stream);
 size_t sparse_attn_workspace_bytes(const AttnArgs &a);
 size_t topk_workspace_bytes(const TopkArgs &a);
+size_t indexer_bwd_workspace_bytes(const IndexerBwdArgs &a);
 
 // Sequence metadata for one sequence, clamped to the host-validated bounds so
 // that inconsistent device offsets can never produce an out-of-bounds access.

@@ -231,10 +231,10 @@ def test_align_loss_shares_the_attention_shape_checks():
     assert "max_kv_len" in _msg()
 
 
-def _ibwd(p, idx=FAKE, grad=FAKE, dq=FAKE, dw=FAKE, dk=FAKE, ld_grad=2048):
+def _ibwd(p, idx=FAKE, grad=FAKE, dq=FAKE, dw=FAKE, dk=FAKE, ld_grad=2048, ws=None, ws_n=0):
     lib = binding.load_library()
     return lib.dsa_indexer_backward(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, idx, grad, ld_grad,
-                                    dq, dw, dk, None)
+                                    dq, dw, dk, ws, ws_n, None)
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -254,3 +254,26 @@ def test_indexer_backward_rejects_bad_arguments(kw, status, needle):
 def test_indexer_backward_shares_the_indexer_shape_checks():
     assert _ibwd(_problem(idx_dim=48)) == binding.DSA_ERR_UNSUPPORTED
     assert _ibwd(_problem(idx_heads=0)) == binding.DSA_ERR_INVALID_ARGUMENT
+
+
+def test_indexer_backward_two_pass_workspace():
+    """Contributions [total_q][k rounded up to 64][128] f32, the ascending key
+    lists [total_q][k rounded up] i32 and the 64-key block starts
+    [total_q][ceil(max_kv_len / 64) + 2] i32, each section 256-byte aligned."""
+    lib = binding.load_library()
+    p = _problem()                      # 4096 rows, k = 2048, max_kv_len = 4096
+    need = lib.dsa_workspace_bytes(ctypes.byref(p), binding.WS_INDEXER_BWD)
+    assert need == 4096 * 2048 * 512 + 4096 * 2048 * 4 + 4096 * (64 + 2) * 4
+    odd = _problem(topk=100, max_kv_len=4000, total_kv=4000)
+    kp, nbr = 128, 4000 // 64 + 1 + 2
+    r = lambda x: (x + 255) // 256 * 256
+    assert lib.dsa_workspace_bytes(ctypes.byref(odd), binding.WS_INDEXER_BWD) == \
+        r(4096 * kp * 512) + r(4096 * kp * 4) + r(4096 * nbr * 4)
+    # the fp32 path for other shapes and a problem with no rows take none
+    assert lib.dsa_workspace_bytes(ctypes.byref(_problem(idx_heads=48, idx_dim=64)),
+                                   binding.WS_INDEXER_BWD) == 0
+    assert lib.dsa_workspace_bytes(ctypes.byref(_problem(total_q=0, max_q_len=0)), binding.WS_INDEXER_BWD) == 0
+    assert _ibwd(p, ws=FAKE, ws_n=need - 1) == binding.DSA_ERR_WORKSPACE
+    assert "indexer backward workspace" in _msg()
+    assert _ibwd(p, ws=FAKE + 4, ws_n=need) == binding.DSA_ERR_INVALID_ARGUMENT
+    assert "aligned" in _msg()

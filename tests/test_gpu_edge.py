@@ -40,9 +40,11 @@ def _inputs(q_lens, kv_lens, seed=1):
     return inp
 
 
-def test_mixed_degenerate_batch_all_entry_points():
+@pytest.mark.parametrize("two_pass", [False, True], ids=["atomic", "two_pass"])
+def test_mixed_degenerate_batch_all_entry_points(two_pass):
+    """Also the two-pass dk: 64-key blocks here straddle several sequences."""
     q_lens, kv_lens = [0, 3, 0, 1, 2, 5], [50, 3, 0, 1, 40, 6]
-    _announce(f"degenerate batch q_lens {q_lens} kv_lens {kv_lens}")
+    _announce(f"degenerate batch q_lens {q_lens} kv_lens {kv_lens} two_pass={two_pass}")
     inp = _inputs(q_lens, kv_lens)
     prob = dsa.Problem.from_workload(WL, inp)
     g = H.to_dev(inp)
@@ -62,8 +64,11 @@ def test_mixed_degenerate_batch_all_entry_points():
     dq = torch.empty(c.total_q, c.idx_heads, c.idx_dim, dtype=torch.float32, device=DEV)
     dw = torch.empty(c.total_q, c.idx_heads, dtype=torch.float32, device=DEV)
     dk = torch.zeros(c.total_kv, c.idx_dim, dtype=torch.float32, device=DEV)
+    ws = None
+    if two_pass:
+        ws = torch.full((dsa.workspace_bytes(prob, dsa.WS_INDEXER_BWD),), 0xFF, dtype=torch.uint8, device=DEV)
     dsa.indexer_backward(prob, g["q_fp8"], g["q_scale"], g["w"], g["k_fp8"], g["k_scale"], grad, dq, dw, dk,
-                         idx=idx)
+                         idx=idx, workspace=ws)
     torch.cuda.synchronize()
 
     rows, positions, kv0s, lens = [], [], [], []
@@ -109,9 +114,12 @@ def test_problems_without_query_rows_write_nothing():
     dsa.sparse_attn(prob, g["q"], g["kv"], torch.empty(0, WL.topk, dtype=torch.int32, device=DEV),
                     torch.empty(0, WL.heads, WL.d_latent, dtype=torch.bfloat16, device=DEV))
     dk = torch.full((20, WL.idx_dim), 3.0, device=DEV)
-    dsa.indexer_backward(prob, g["q_fp8"], g["q_scale"], g["w"], g["k_fp8"], g["k_scale"],
-                         torch.empty(0, WL.topk, device=DEV), torch.empty(0, WL.idx_heads, WL.idx_dim, device=DEV),
-                         torch.empty(0, WL.idx_heads, device=DEV), dk,
-                         idx=torch.empty(0, WL.topk, dtype=torch.int32, device=DEV))
+    assert dsa.workspace_bytes(prob, dsa.WS_INDEXER_BWD) == 0
+    for ws in (None, torch.empty(16, dtype=torch.uint8, device=DEV)):
+        dsa.indexer_backward(prob, g["q_fp8"], g["q_scale"], g["w"], g["k_fp8"], g["k_scale"],
+                             torch.empty(0, WL.topk, device=DEV),
+                             torch.empty(0, WL.idx_heads, WL.idx_dim, device=DEV),
+                             torch.empty(0, WL.idx_heads, device=DEV), dk,
+                             idx=torch.empty(0, WL.topk, dtype=torch.int32, device=DEV), workspace=ws)
     torch.cuda.synchronize()
     assert bool((dk == 3.0).all())     # dk is only ever added to, and here by nothing

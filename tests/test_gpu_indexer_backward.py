@@ -6,10 +6,12 @@ own gradient; indices come from the library's top-k on seeded inputs, or are
 built in the test.  dq and dw are compared row by row, dk (accumulated by
 atomics over every row) key by key, within the bounds in tests/gpu_helpers.py.
 Covered: the MFMA path (H_I = 64, d_I = 128) in both forms with ragged last
-tiles, -1 entries anywhere and an empty row; two chunk calls adding into one
-dk; the fp32 path for other shapes; and sampled rows of the last chunk of the
-128K prefill (with the gradient zero outside the sampled rows, so that dk is
-known exactly)."""
+tiles, -1 entries anywhere (in any order) and an empty row; two chunk calls
+adding into one dk; the fp32 path for other shapes; sampled rows of the last
+chunk of the 128K prefill (with the gradient zero outside the sampled rows, so
+that dk is known exactly); and a sequence longer than the two-pass
+reduction's 4096-row scan window.  Every sparse MFMA case runs with dk by
+atomics and with the two-pass dk (a workspace given)."""
 import numpy as np
 import pytest
 import torch
@@ -36,14 +38,24 @@ def _topk(prob, g):
     return scores, idx
 
 
-def _backward(prob, g, grad, idx, dk=None):
+def _workspace(prob, two_pass):
+    """The two-pass workspace, filled with NaN bytes: nothing may read what
+    the call did not write."""
+    if not two_pass:
+        return None
+    n = dsa.workspace_bytes(prob, dsa.WS_INDEXER_BWD)
+    assert n > 0
+    return torch.full((n,), 0xFF, dtype=torch.uint8, device=DEV)
+
+
+def _backward(prob, g, grad, idx, dk=None, two_pass=False):
     c = prob.c
     dq = torch.full((c.total_q, c.idx_heads, c.idx_dim), float("nan"), dtype=torch.float32, device=DEV)
     dw = torch.full((c.total_q, c.idx_heads), float("nan"), dtype=torch.float32, device=DEV)
     if dk is None:
         dk = torch.zeros(c.total_kv, c.idx_dim, dtype=torch.float32, device=DEV)
     dsa.indexer_backward(prob, g["q_fp8"], g["q_scale"], g["w"], g["k_fp8"], g["k_scale"], grad, dq, dw,
-                         dk, idx=idx)
+                         dk, idx=idx, workspace=_workspace(prob, two_pass))
     torch.cuda.synchronize()
     return dq, dw, dk
 
@@ -65,10 +77,14 @@ def _check(inp, prob, rows, positions, kv0s, grad, idx, dq, dw, dk, all_rows=Tru
         assert not dkg[untouched].any(), "dk rows no row selected must stay zero"
 
 
+TWO_PASS = pytest.mark.parametrize("two_pass", [False, True], ids=["atomic", "two_pass"])
+
+
+@TWO_PASS
 @pytest.mark.parametrize("seed", [0, 1])
-def test_backward_sparse_mfma(seed):
+def test_backward_sparse_mfma(seed, two_pass):
     wl = MED
-    _announce(f"indexer backward sparse L={wl.seq_len} k={wl.topk} seed={seed}")
+    _announce(f"indexer backward sparse L={wl.seq_len} k={wl.topk} seed={seed} two_pass={two_pass}")
     inp = wk.generate(wl)
     prob = dsa.Problem.from_workload(wl, inp)
     g = H.to_dev(inp)
@@ -76,12 +92,13 @@ def test_backward_sparse_mfma(seed):
     gen = torch.Generator(device="cpu").manual_seed(100 + seed)
     grad = (torch.randn(prob.total_q, wl.topk, generator=gen) * 1e-3).to(DEV)
     grad[idx < 0] = float("nan")        # entries past the selection are never read
-    dq, dw, dk = _backward(prob, g, grad, idx)
+    dq, dw, dk = _backward(prob, g, grad, idx, two_pass=two_pass)
     L = wl.seq_len
     _check(inp, prob, list(range(L)), list(range(L)), [0] * L, torch.nan_to_num(grad), idx, dq, dw, dk)
 
 
 def test_backward_dense_mfma():
+    """The dense form ignores a workspace (its pairs are all causal keys)."""
     wl = MED.scaled(seq_len=300)
     _announce("indexer backward dense L=300")
     inp = wk.generate(wl)
@@ -92,14 +109,17 @@ def test_backward_dense_mfma():
     grad = torch.randn(prob.total_q, ld, generator=gen) * 1e-3
     for r in range(300):
         grad[r, r + 1:] = float("nan")   # past pos: never read
-    dq, dw, dk = _backward(prob, g, grad.to(DEV), None)
+    dq, dw, dk = _backward(prob, g, grad.to(DEV), None, two_pass=True)
     L = wl.seq_len
     _check(inp, prob, list(range(L)), list(range(L)), [0] * L, torch.nan_to_num(grad), None, dq, dw, dk)
 
 
-def test_backward_custom_indices_gaps_and_empty_row():
+@TWO_PASS
+def test_backward_custom_indices_gaps_and_empty_row(two_pass):
+    """Indices in random order (the two-pass form sorts them), k = 80 (not a
+    multiple of the 64-key tile)."""
     wl = MED.scaled(seq_len=400, topk=80)
-    _announce("indexer backward sparse, -1 anywhere, empty row")
+    _announce(f"indexer backward sparse, -1 anywhere, empty row, two_pass={two_pass}")
     inp = wk.generate(wl)
     prob = dsa.Problem.from_workload(wl, inp)
     g = H.to_dev(inp)
@@ -112,29 +132,30 @@ def test_backward_custom_indices_gaps_and_empty_row():
     idx_np[5] = -1
     idx = torch.as_tensor(idx_np, device=DEV)
     grad = torch.as_tensor(rng.standard_normal((L, k)) * 1e-3, dtype=torch.float32, device=DEV)
-    dq, dw, dk = _backward(prob, g, grad, idx)
+    dq, dw, dk = _backward(prob, g, grad, idx, two_pass=two_pass)
     _check(inp, prob, list(range(L)), list(range(L)), [0] * L, grad, idx, dq, dw, dk)
     assert not dq[5].any() and not dw[5].any()
 
 
-def test_backward_chunks_add_into_one_dk():
+@TWO_PASS
+def test_backward_chunks_add_into_one_dk(two_pass):
     """Two chunk calls (rows [0, 300) and [300, 600)) adding into one dk give
     the single call's dk."""
     wl = MED.scaled(seq_len=600)
-    _announce("indexer backward, two chunks into one dk")
+    _announce(f"indexer backward, two chunks into one dk, two_pass={two_pass}")
     inp = wk.generate(wl)
     g = H.to_dev(inp)
     prob = dsa.Problem.from_workload(wl, inp)
     _, idx = _topk(prob, g)
     gen = torch.Generator(device="cpu").manual_seed(3)
     grad = (torch.randn(600, wl.topk, generator=gen) * 1e-3).to(DEV)
-    dq, dw, dk_all = _backward(prob, g, grad, idx)
+    dq, dw, dk_all = _backward(prob, g, grad, idx, two_pass=two_pass)
     dk = torch.zeros_like(dk_all)
     for r0, r1 in ((0, 300), (300, 600)):
         sub = {key: (v[r0:r1] if key in ("q_fp8", "q_scale", "w", "q") else v) for key, v in g.items()}
         pc = dsa.Problem.from_workload(wl, inp, q_rows=slice(r0, r1), q_pos0=r0)
         sub["k_fp8"], sub["k_scale"] = g["k_fp8"][:r1], g["k_scale"][:r1]
-        _backward(pc, sub, grad[r0:r1].contiguous(), idx[r0:r1].contiguous(), dk=dk[:r1])
+        _backward(pc, sub, grad[r0:r1].contiguous(), idx[r0:r1].contiguous(), dk=dk[:r1], two_pass=two_pass)
     # both dk are checked against the oracle over every row
     _check(inp, prob, list(range(600)), list(range(600)), [0] * 600, grad, idx, dq, dw, dk)
     _check(inp, prob, list(range(600)), list(range(600)), [0] * 600, grad, idx, dq, dw, dk_all)
@@ -159,11 +180,12 @@ def test_backward_fp32_path(wl):
     _check(inp, prob, list(range(L)), list(range(L)), [0] * L, gd, None, dq, dw, dk)
 
 
-def test_backward_of_the_alignment_loss_gradient():
+@TWO_PASS
+def test_backward_of_the_alignment_loss_gradient(two_pass):
     """The composed training step: the alignment loss's gradient on the
     scores carried back through the indexer."""
     wl = MED.scaled(seq_len=500)
-    _announce("indexer backward of the alignment loss gradient")
+    _announce(f"indexer backward of the alignment loss gradient, two_pass={two_pass}")
     inp = wk.generate(wl)
     prob = dsa.Problem.from_workload(wl, inp)
     g = H.to_dev(inp)
@@ -175,17 +197,18 @@ def test_backward_of_the_alignment_loss_gradient():
     loss = torch.empty(c.total_q, dtype=torch.float32, device=DEV)
     grad = torch.empty(c.total_q, c.topk, dtype=torch.float32, device=DEV)
     dsa.indexer_align_loss(prob, g["q"], g["kv"], lse, scores, loss, grad, idx=idx)
-    dq, dw, dk = _backward(prob, g, grad, idx)
+    dq, dw, dk = _backward(prob, g, grad, idx, two_pass=two_pass)
     L = wl.seq_len
     _check(inp, prob, list(range(L)), list(range(L)), [0] * L, grad, idx, dq, dw, dk)
 
 
-def test_backward_last_chunk_of_128k_prefill():
+@TWO_PASS
+def test_backward_last_chunk_of_128k_prefill(two_pass):
     """The launch a training step makes per chunk, at full size: the last
     4096-row chunk against the 131072-key prefix.  The gradient is nonzero on
     a few sampled rows only, so dk is exactly their contribution."""
     wl = wk.CHUNKED_PREFILL_128K
-    _announce("indexer backward 128K prefill, last chunk")
+    _announce(f"indexer backward 128K prefill, last chunk, two_pass={two_pass}")
     inp = wk.generate(wl, device=DEV)
     L, C = wl.seq_len, wl.chunk
     r0 = L - C
@@ -201,6 +224,33 @@ def test_backward_last_chunk_of_128k_prefill():
     grad = torch.zeros(C, wl.topk)
     grad[rows] = torch.randn(len(rows), wl.topk, generator=gen) * 1e-3
     grad = grad.to(DEV)
-    dq, dw, dk = _backward(prob, sub, grad, idx)
+    dq, dw, dk = _backward(prob, sub, grad, idx, two_pass=two_pass)
     assert torch.isfinite(dq).all() and torch.isfinite(dw).all()
     _check(sub, prob, rows, [r0 + r for r in rows], [0] * len(rows), grad, idx, dq, dw, dk)
+
+
+def test_backward_two_pass_past_one_scan_window():
+    """4600 rows in one call: the reduction scans a sequence's rows 4096 at a
+    time.  The gradient is nonzero on sampled rows on both sides of the
+    window boundary (dk then exactly theirs, against the oracle); with the
+    gradient on every row, the two-pass dk and the atomic one agree to fp32
+    summation order."""
+    wl = MED.scaled(seq_len=4600, heads=16)
+    _announce("indexer backward two-pass, 4600 rows")
+    inp = wk.generate(wl)
+    prob = dsa.Problem.from_workload(wl, inp)
+    g = H.to_dev(inp)
+    _, idx = _topk(prob, g)
+    L = wl.seq_len
+    rows = [0, 1000, 4095, 4096, 4097, 4599]
+    gen = torch.Generator(device="cpu").manual_seed(21)
+    grad = torch.zeros(L, wl.topk)
+    grad[rows] = torch.randn(len(rows), wl.topk, generator=gen) * 1e-3
+    dq, dw, dk = _backward(prob, g, grad.to(DEV), idx, two_pass=True)
+    _check(inp, prob, rows, rows, [0] * len(rows), grad, idx, dq, dw, dk)
+    full = (torch.randn(L, wl.topk, generator=gen) * 1e-3).to(DEV)
+    _, _, dk_a = _backward(prob, g, full, idx)
+    _, _, dk_t = _backward(prob, g, full, idx, two_pass=True)
+    scale = dk_a.abs().max().item()
+    assert scale > 0
+    assert (dk_t - dk_a).abs().max().item() <= 1e-5 * scale
