@@ -186,6 +186,9 @@ class ChunkedPrefill:
             self.dq = torch.empty(wl.chunk, wl.idx_heads, wl.idx_dim, dtype=torch.float32, device=dev)
             self.dw = torch.empty(wl.chunk, wl.idx_heads, dtype=torch.float32, device=dev)
             self.dk = torch.zeros(wl.seq_len, wl.idx_dim, dtype=torch.float32, device=dev)
+            # the indexer backward's two-pass dk (the largest chunk's size serves all)
+            n = max(dsa.workspace_bytes(prob, dsa.WS_INDEXER_BWD) for _, _, prob in self.chunks)
+            self.bwd_ws = torch.empty(n, dtype=torch.uint8, device=dev)
         self.dk.zero_()
         for ci, (r0, sl, prob) in enumerate(self.chunks):
             rows = sl.stop - sl.start
@@ -204,7 +207,8 @@ class ChunkedPrefill:
                 events[ci][1].record()
             dsa.indexer_backward(prob, inp["q_fp8"][sl], inp["q_scale"][sl], inp["w"][sl],
                                  inp["k_fp8"][: sl.stop], inp["k_scale"][: sl.stop], self.grad[:rows],
-                                 self.dq[:rows], self.dw[:rows], self.dk[: sl.stop], idx=self.idx[sl])
+                                 self.dq[:rows], self.dw[:rows], self.dk[: sl.stop], idx=self.idx[sl],
+                                 workspace=self.bwd_ws)
             if events is not None:
                 events[ci][2].record()
 

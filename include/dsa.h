@@ -271,9 +271,11 @@ dsa_status dsa_indexer_align_loss(const dsa_problem *p, const uint16_t *q, const
  *         dsa_workspace_bytes(p, DSA_WS_INDEXER_BWD) bytes (16-byte aligned;
  *         about total_q * k * 516 bytes) selects the faster two-pass form:
  *         each (row, key) contribution is stored there and a second kernel
- *         sums them per block of 64 keys and adds the sums to dk (no atomics
- *         to memory).  Its contents need no initialisation and are
- *         overwritten.  Other forms ignore it.  Too small: DSA_ERR_WORKSPACE.
+ *         sums them per key, 64 keys per workgroup, and adds the sums to dk
+ *         (about one atomic per dk element per 4096 rows instead of one per
+ *         row that selected the key).  Its contents need no initialisation
+ *         and are overwritten.  Other forms ignore it.  Too small:
+ *         DSA_ERR_WORKSPACE.  dk must be ordinary device memory either way.
  * Calls that overlap on one stream's timeline and add into the same dk rows
  * must be ordered by the caller (the two-pass form reads and writes dk).
  */

@@ -28,13 +28,14 @@
 //    collide.  Without a workspace each tile's block is added to dk with
 //    fp32 atomics; these are resolved beyond the L2 (about one 4-byte write
 //    to HBM per atomic), which makes them the kernel's bound.  With one
-//    (sparse form), dk is formed in two passes with no atomics to memory:
-//    the token kernel stores each (token, key) contribution, 128 floats, at
-//    the key's rank in the token's ascending key list, along with that list
-//    and, per 64-key block of the sequence, where the block's keys start in
-//    it; then one workgroup per 64-key block gathers the contributions to
-//    its keys from every token of the sequence, adds them in LDS and adds
-//    the sums to dk once.
+//    (sparse form), dk is formed in two passes: the token kernel stores each
+//    (token, key) contribution, 128 floats, at the key's rank in the token's
+//    ascending key list, along with that list and, per 64-key block of the
+//    sequence, where the block's keys start in it; then one workgroup per
+//    64-key block gathers the contributions to its keys from every token of
+//    the sequence, sums them per key in registers and adds the sums to dk
+//    (about one atomic per dk element and 4096 tokens instead of one per
+//    token that selected the key).
 #include <climits>
 
 #include "common.h"
@@ -441,26 +442,29 @@ __global__ __launch_bounds__(kBT8) void indexer_bwd_kernel(IndexerBwdArgs p) {
 // its ascending key list is exactly its keys in the block, so an exclusive
 // scan of the run lengths numbers the window's (token, key) pairs.  Pairs
 // are then handled kRCap at a time: every token writes its index over its
-// run (pair -> token), every pair's key is read once, and half-wave h, which
-// owns the block's keys 4h .. 4h+3, picks its pairs out by ballot and sums
-// their 128 floats in registers, kRU pairs in flight.  No two half-waves
-// touch one key, so nothing is atomic; at the end each adds its four rows to
-// dk.  Workgroup ids are laid out so that consecutive blocks run on one XCD
-// and share the bnd lines in its L2.
+// run (pair -> token), every pair's key and contribution offset are found
+// once, and a counting sort by key lays the offsets out key by key.  The
+// sorted pairs are split evenly over the 16 half-waves (key popularity
+// varies, so a split by key would leave most of them waiting for one); each
+// walks its slice, kRU pairs in flight, summing a run of one key's pairs in
+// registers and adding the run's 128 sums to the key's dk row when the key
+// changes -- an fp32 atomic, since a key's run can straddle two slices, but
+// about one per key and batch instead of one per (token, key) pair.
+// Workgroup ids are laid out so that consecutive blocks run on one XCD and
+// share the bnd lines in its L2.
 constexpr int kRWin = 4096;            // tokens per scan window
-constexpr int kRCap = 8192;            // pairs per batch
+constexpr int kRCap = 4096;            // pairs per batch
 constexpr int kRT = 512;
-constexpr int kRHW = kRT / 32;         // half-waves, each owning kRKB / kRHW keys
-constexpr int kRChunk = 256;           // pair slots a half-wave scans at a time
-constexpr int kRU = 4;
-static_assert(kRKB == 4 * kRHW, "four keys per half-wave");
+constexpr int kRHW = kRT / 32;         // half-waves
+constexpr int kRU = 8;
+static_assert(kRCap % kRT == 0, "whole pair slots per thread");
 
 __global__ __launch_bounds__(kRT) void dk_reduce_kernel(IndexerBwdArgs p, int nblk, int per) {
-  constexpr int D = 128;
-  __shared__ int s_lo[kRWin], s_ex[kRWin];
+  constexpr int D = 128, PER = kRCap / kRT;
+  __shared__ int s_lo[kRWin], s_ex[kRWin + 1];
   __shared__ uint16_t s_row[kRCap];
-  __shared__ uint8_t s_key[kRCap];
-  __shared__ uint16_t s_list[kRHW][kRChunk];
+  __shared__ int s_soff[kRCap];          // (token - w0) * kpad + rank, sorted by key
+  __shared__ int s_bin[kRKB + 1], s_cur[kRKB];
   __shared__ int s_wsum[kRT / 64];
   __shared__ int s_b0;
   const int wid = __builtin_amdgcn_workgroup_id_x();
@@ -471,12 +475,6 @@ __global__ __launch_bounds__(kRT) void dk_reduce_kernel(IndexerBwdArgs p, int nb
   const int hw = tid >> 5, l32 = tid & 31;
   const int64_t G0 = (int64_t)j * kRKB;
   const int64_t G1 = G0 + kRKB < p.seq.total_kv ? G0 + kRKB : p.seq.total_kv;
-  // this half-wave's sums: key 4*hw + kk, dims l32 + 32*q
-  float acc[4][4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) acc[kk][q] = 0.f;
   // first sequence whose keys end after G0 (key offsets are non-decreasing)
   if (wave == 0) {
     int cnt = 0;
@@ -496,7 +494,7 @@ __global__ __launch_bounds__(kRT) void dk_reduce_kernel(IndexerBwdArgs p, int nb
     for (int64_t w0 = s.q0; w0 < s.q1; w0 += kRWin) {
       const int nrow = (int)(s.q1 - w0 < kRWin ? s.q1 - w0 : kRWin);
       // thread: tokens 8*tid .. +7 of the window; runs clamped into [0, kpad]
-      int lo8[8], len8[8], ex8[8], sum = 0;
+      int lo8[8], len8[8], sum = 0;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int i = 8 * tid + e;
@@ -525,81 +523,113 @@ __global__ __launch_bounds__(kRT) void dk_reduce_kernel(IndexerBwdArgs p, int nb
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int i = 8 * tid + e;
-        ex8[e] = before;
         if (i < nrow) {
           s_lo[i] = lo8[e];
           s_ex[i] = before;
         }
         before += len8[e];
       }
+      if (tid == 0) s_ex[nrow] = P;
+      __syncthreads();
+      const int64_t cbase = w0 * p.kpad;
       for (int P0 = 0; P0 < P; P0 += kRCap) {
         const int np = P - P0 < kRCap ? P - P0 : kRCap;
         // pair -> token over this batch
-#pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int x0 = ex8[e] > P0 ? ex8[e] : P0;
-          const int x1 = ex8[e] + len8[e] < P0 + np ? ex8[e] + len8[e] : P0 + np;
-          for (int x = x0; x < x1; ++x) s_row[x - P0] = (uint16_t)(8 * tid + e);
+          const int i = 8 * tid + e;
+          if (i >= nrow) break;
+          const int a = s_ex[i], b2 = s_ex[i + 1];
+          const int x0 = a > P0 ? a : P0;
+          const int x1 = b2 < P0 + np ? b2 : P0 + np;
+          for (int x = x0; x < x1; ++x) s_row[x - P0] = (uint16_t)i;
         }
+        if (tid < kRKB) s_bin[tid] = 0;
         __syncthreads();
-        // each pair's key, as an index into the block (255: not in it)
-#pragma unroll 4
-        for (int x = tid; x < np; x += kRT) {
-          const int i = s_row[x];
-          const int64_t e = (w0 + i) * p.kpad + s_lo[i] + (P0 + x - s_ex[i]);
-          const int64_t l = s.kv0 + p.skey[e] - G0;
-          s_key[x] = (l >= 0 && l < kRKB) ? (uint8_t)l : (uint8_t)255;
-        }
-        __syncthreads();
-        for (int base = 0; base < np; base += kRChunk) {
-          // this half-wave's pairs among slots base .. base + kRChunk - 1
-          int cnt = 0;
+        // each pair's contribution offset and key (an index into the block;
+        // -1: not in it), then the key histogram
+        int off8[PER], key8[PER];
 #pragma unroll
-          for (int s2 = 0; s2 < kRChunk; s2 += 32) {
-            const int x = base + s2 + l32;
-            const int kk = x < np ? s_key[x] : 255;
-            const bool mine = (kk >> 2) == hw;
-            const uint32_t bits = (uint32_t)(__ballot(mine) >> (lane & 32));
-            if (mine) s_list[hw][cnt + __popc(bits & ((1u << l32) - 1))] = (uint16_t)x;
-            cnt += __popc(bits);
+        for (int r = 0; r < PER; ++r) {
+          const int x = tid + kRT * r;
+          key8[r] = -1;
+          off8[r] = 0;
+          if (x < np) {
+            const int i = s_row[x];
+            off8[r] = i * p.kpad + s_lo[i] + (P0 + x - s_ex[i]);
+            const int64_t l = s.kv0 + p.skey[cbase + off8[r]] - G0;
+            key8[r] = (l >= 0 && l < kRKB) ? (int)l : -1;
           }
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-          for (int q0 = 0; q0 < cnt; q0 += kRU) {
+        }
+#pragma unroll
+        for (int r = 0; r < PER; ++r)
+          if (key8[r] >= 0) __hip_atomic_fetch_add(&s_bin[key8[r]], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __syncthreads();
+        if (wave == 0) {
+          const int c = lane < kRKB ? s_bin[lane] : 0;
+          const int incl = (int)wave_scan<0>((uint32_t)c);
+          if (lane < kRKB) {
+            s_bin[lane] = incl - c;
+            s_cur[lane] = incl - c;
+          }
+          if (lane == kRKB - 1) s_bin[kRKB] = incl;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < PER; ++r)
+          if (key8[r] >= 0) {
+            const int at = __hip_atomic_fetch_add(&s_cur[key8[r]], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            s_soff[at] = off8[r];
+          }
+        __syncthreads();
+        // this half-wave's slice [x0, x1) of the sorted pairs; key of slot x:
+        // the last key with s_bin[key] <= x
+        const int T = s_bin[kRKB];
+        const int x0 = T * hw / kRHW, x1 = T * (hw + 1) / kRHW;
+        if (x0 < x1) {
+          int key = 0;
+#pragma unroll
+          for (int st = kRKB / 2; st >= 1; st >>= 1)
+            if (s_bin[key + st] <= x0) key += st;
+          int next = s_bin[key + 1];
+          float run[4] = {0.f, 0.f, 0.f, 0.f};
+          auto flush = [&]() {
+            float *dst = p.dk + (G0 + key) * D + l32;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              unsafeAtomicAdd(dst + 32 * q, run[q]);
+              run[q] = 0.f;
+            }
+          };
+          for (int base = x0; base < x1; base += kRU) {
             float v[kRU][4];
-            int kl[kRU];
 #pragma unroll
             for (int u = 0; u < kRU; ++u) {
-              const int x = s_list[hw][q0 + u < cnt ? q0 + u : cnt - 1];
-              const int i = s_row[x];
-              const int64_t e = (w0 + i) * p.kpad + s_lo[i] + (P0 + x - s_ex[i]);
-              const float *src = p.contrib + e * D + l32;
+              const int xi = base + u < x1 ? base + u : x1 - 1;
+              const float *src = p.contrib + (cbase + s_soff[xi]) * D + l32;
 #pragma unroll
               for (int q = 0; q < 4; ++q) v[u][q] = __builtin_nontemporal_load(src + 32 * q);
-              kl[u] = q0 + u < cnt ? (s_key[x] & 3) : -1;
             }
 #pragma unroll
-            for (int u = 0; u < kRU; ++u)
+            for (int u = 0; u < kRU; ++u) {
+              const int xi = base + u;
+              if (xi < x1) {
+                if (xi >= next) {   // a new key (keys with no pairs are skipped)
+                  flush();
+                  do {
+                    ++key;
+                    next = s_bin[key + 1];
+                  } while (xi >= next);
+                }
 #pragma unroll
-              for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) acc[kk][q] += kl[u] == kk ? v[u][q] : 0.f;
+                for (int q = 0; q < 4; ++q) run[q] += v[u][q];
+              }
+            }
           }
-          __builtin_amdgcn_wave_barrier();   // s_list is rewritten by the next chunk
+          flush();
         }
-        __syncthreads();   // s_row and s_key are rewritten by the next batch
+        __syncthreads();   // s_row, s_bin and s_soff are rewritten by the next batch
       }
       __syncthreads();     // the next window rewrites s_lo, s_ex and s_wsum
-    }
-  }
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int64_t row = G0 + 4 * hw + kk;
-    if (row < G1) {
-      float *dst = p.dk + row * D + l32;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) dst[32 * q] += acc[kk][q];
     }
   }
 }
