@@ -449,7 +449,9 @@ __global__ __launch_bounds__(kBT8) void indexer_bwd_kernel(IndexerBwdArgs p) {
 // walks its slice, kRU pairs in flight, summing a run of one key's pairs in
 // registers and adding the run's 128 sums to the key's dk row when the key
 // changes -- an fp32 atomic, since a key's run can straddle two slices, but
-// about one per key and batch instead of one per (token, key) pair.
+// about one per key and batch instead of one per (token, key) pair.  With
+// few blocks (an early chunk of a long prefill) each block's tokens are
+// split over nsplit workgroups, so that the grid still fills the chip.
 // Workgroup ids are laid out so that consecutive blocks run on one XCD and
 // share the bnd lines in its L2.
 constexpr int kRWin = 4096;            // tokens per scan window
@@ -459,7 +461,7 @@ constexpr int kRHW = kRT / 32;         // half-waves
 constexpr int kRU = 8;
 static_assert(kRCap % kRT == 0, "whole pair slots per thread");
 
-__global__ __launch_bounds__(kRT) void dk_reduce_kernel(IndexerBwdArgs p, int nblk, int per) {
+__global__ __launch_bounds__(kRT) void dk_reduce_kernel(IndexerBwdArgs p, int nblk, int nsplit, int per) {
   constexpr int D = 128, PER = kRCap / kRT;
   __shared__ int s_lo[kRWin], s_ex[kRWin + 1];
   __shared__ uint16_t s_row[kRCap];
@@ -468,7 +470,8 @@ __global__ __launch_bounds__(kRT) void dk_reduce_kernel(IndexerBwdArgs p, int nb
   __shared__ int s_wsum[kRT / 64];
   __shared__ int s_b0;
   const int wid = __builtin_amdgcn_workgroup_id_x();
-  const int j = (wid & 7) * per + (wid >> 3);
+  const int lin = (wid & 7) * per + (wid >> 3);
+  const int j = lin / nsplit, split = lin - j * nsplit;
   if (j >= nblk) return;
   const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -491,8 +494,11 @@ __global__ __launch_bounds__(kRT) void dk_reduce_kernel(IndexerBwdArgs p, int nb
     if (s.kv0 >= G1) break;
     if (s.kvlen == 0 || s.kv0 + s.kvlen <= G0) continue;
     const int jl = (int)(j - s.kv0 / kRKB);   // 0 <= jl < the sequence's block count
-    for (int64_t w0 = s.q0; w0 < s.q1; w0 += kRWin) {
-      const int nrow = (int)(s.q1 - w0 < kRWin ? s.q1 - w0 : kRWin);
+    // this workgroup's share of the sequence's tokens
+    const int64_t nq = s.q1 - s.q0;
+    const int64_t qa = s.q0 + nq * split / nsplit, qb = s.q0 + nq * (split + 1) / nsplit;
+    for (int64_t w0 = qa; w0 < qb; w0 += kRWin) {
+      const int nrow = (int)(qb - w0 < kRWin ? qb - w0 : kRWin);
       // thread: tokens 8*tid .. +7 of the window; runs clamped into [0, kpad]
       int lo8[8], len8[8], sum = 0;
 #pragma unroll
@@ -789,9 +795,13 @@ hipError_t launch_indexer_backward(const IndexerBwdArgs &a0, hipStream_t stream)
       a.nbr = w.nbr;
       hipLaunchKernelGGL((indexer_bwd_kernel<false, true>), grid, dim3(kBT8), 0, stream, a);
       if (a.seq.total_kv > 0) {
+        // at least about 2048 workgroups (two per CU, four rounds) when the
+        // blocks alone are fewer
         const int nblk = (int)((a.seq.total_kv + kRKB - 1) / kRKB);
-        const int per = (nblk + 7) / 8;
-        hipLaunchKernelGGL(dk_reduce_kernel, dim3(8 * (unsigned)per), dim3(kRT), 0, stream, a, nblk, per);
+        int nsplit = (2048 + nblk - 1) / nblk;
+        nsplit = nsplit > 64 ? 64 : nsplit;
+        const int per = (int)(((int64_t)nblk * nsplit + 7) / 8);
+        hipLaunchKernelGGL(dk_reduce_kernel, dim3(8 * (unsigned)per), dim3(kRT), 0, stream, a, nblk, nsplit, per);
       }
     } else {
       hipLaunchKernelGGL((indexer_bwd_kernel<false, false>), grid, dim3(kBT8), 0, stream, a);

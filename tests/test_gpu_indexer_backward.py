@@ -230,27 +230,62 @@ def test_backward_last_chunk_of_128k_prefill(two_pass):
 
 
 def test_backward_two_pass_past_one_scan_window():
-    """4600 rows in one call: the reduction scans a sequence's rows 4096 at a
-    time.  The gradient is nonzero on sampled rows on both sides of the
-    window boundary (dk then exactly theirs, against the oracle); with the
-    gradient on every row, the two-pass dk and the atomic one agree to fp32
-    summation order."""
-    wl = MED.scaled(seq_len=4600, heads=16)
-    _announce("indexer backward two-pass, 4600 rows")
-    inp = wk.generate(wl)
-    prob = dsa.Problem.from_workload(wl, inp)
-    g = H.to_dev(inp)
-    _, idx = _topk(prob, g)
-    L = wl.seq_len
+    """4600 query rows against the 131072-key prefix in one call: the
+    reduction takes a block's tokens 4096 at a time (with 2048 key blocks
+    each block has one workgroup).  The gradient is nonzero on sampled rows
+    on both sides of the window boundary, so dk is exactly theirs, against
+    the oracle; with the gradient on every row, the two-pass dk and the
+    atomic one agree to fp32 summation order."""
+    wl = wk.CHUNKED_PREFILL_128K
+    _announce("indexer backward two-pass, last 4600 rows of the 128K prefill")
+    inp = wk.generate(wl, device=DEV)
+    L, n = wl.seq_len, 4600
+    r0 = L - n
+    sl = slice(r0, L)
+    prob = dsa.Problem.from_workload(wl, inp, device=DEV, q_rows=sl, q_pos0=r0)
+    sub = dict(inp)
+    for key in ("q_fp8", "q_scale", "w", "q"):
+        sub[key] = inp[key][sl]
+    _, idx = _topk(prob, sub)
     rows = [0, 1000, 4095, 4096, 4097, 4599]
     gen = torch.Generator(device="cpu").manual_seed(21)
-    grad = torch.zeros(L, wl.topk)
+    grad = torch.zeros(n, wl.topk)
     grad[rows] = torch.randn(len(rows), wl.topk, generator=gen) * 1e-3
-    dq, dw, dk = _backward(prob, g, grad.to(DEV), idx, two_pass=True)
-    _check(inp, prob, rows, rows, [0] * len(rows), grad, idx, dq, dw, dk)
-    full = (torch.randn(L, wl.topk, generator=gen) * 1e-3).to(DEV)
-    _, _, dk_a = _backward(prob, g, full, idx)
-    _, _, dk_t = _backward(prob, g, full, idx, two_pass=True)
+    dq, dw, dk = _backward(prob, sub, grad.to(DEV), idx, two_pass=True)
+    _check(sub, prob, rows, [r0 + r for r in rows], [0] * len(rows), grad, idx, dq, dw, dk)
+    full = (torch.randn(n, wl.topk, generator=gen) * 1e-3).to(DEV)
+    _, _, dk_a = _backward(prob, sub, full, idx)
+    _, _, dk_t = _backward(prob, sub, full, idx, two_pass=True)
+    scale = dk_a.abs().max().item()
+    assert scale > 0
+    assert (dk_t - dk_a).abs().max().item() <= 1e-5 * scale
+
+
+def test_backward_two_pass_first_chunk_split_blocks():
+    """The first 4096-row chunk of the 128K prefill: 64 key blocks, so each
+    block's rows are split over 32 reduction workgroups that add into the
+    same dk rows.  Against the atomic path (itself checked against the
+    oracle above) on every row, and against the oracle on sampled rows."""
+    wl = wk.CHUNKED_PREFILL_128K
+    _announce("indexer backward two-pass, first 128K chunk (split blocks)")
+    inp = wk.generate(wl, device=DEV)
+    C = wl.chunk
+    sl = slice(0, C)
+    prob = dsa.Problem.from_workload(wl, inp, device=DEV, q_rows=sl, q_pos0=0)
+    sub = dict(inp)
+    for key in ("q_fp8", "q_scale", "w", "q"):
+        sub[key] = inp[key][sl]
+    sub["k_fp8"], sub["k_scale"] = inp["k_fp8"][:C], inp["k_scale"][:C]
+    _, idx = _topk(prob, sub)
+    rows = [0, 5, 2047, 2048, 3000, 4095]
+    gen = torch.Generator(device="cpu").manual_seed(23)
+    grad = torch.zeros(C, wl.topk)
+    grad[rows] = torch.randn(len(rows), wl.topk, generator=gen) * 1e-3
+    dq, dw, dk = _backward(prob, sub, grad.to(DEV), idx, two_pass=True)
+    _check(sub, prob, rows, rows, [0] * len(rows), grad, idx, dq, dw, dk)
+    full = (torch.randn(C, wl.topk, generator=gen) * 1e-3).to(DEV)
+    _, _, dk_a = _backward(prob, sub, full, idx)
+    _, _, dk_t = _backward(prob, sub, full, idx, two_pass=True)
     scale = dk_a.abs().max().item()
     assert scale > 0
     assert (dk_t - dk_a).abs().max().item() <= 1e-5 * scale
