@@ -44,7 +44,7 @@
 namespace dsa {
 namespace {
 
-constexpr int kBT = 256;        // threads per workgroup
+constexpr int kBT = 256;        // threads per workgroup (fp32 path)
 constexpr int kBKeys = 64;      // keys per tile
 constexpr int kBMaxK = 4096;
 
@@ -94,12 +94,12 @@ __device__ __forceinline__ v8bf lds_v8bf(const DSA_LDS uint8_t *p) {
   return __builtin_bit_cast(v8bf, *reinterpret_cast<const DSA_LDS v4i *>(p));
 }
 
-// Eight waves, two per SIMD: the dk atomics of a wave fill its in-order
-// vector-memory counter, so a wave that has issued them cannot wait for its
-// next key tile without waiting for them as well; with two waves per SIMD the
-// other one computes meanwhile.  Wave w: z and E for keys 16(w%4).. and head
-// blocks 2(w/4), 2(w/4)+1; dq for heads 16(w%4).. and dims 64(w/4)..; the dk
-// block for keys 16(w%4).. and dims 64(w/4)..
+// Eight waves, two per SIMD, so that one wave's MFMAs can run while the
+// other waits on LDS, on its key loads or (atomic form) on its dk atomics,
+// which share the in-order vector-memory counter with those loads.  Wave w:
+// z and E for keys 16(w%4).. and head blocks 2(w/4), 2(w/4)+1; dq for heads
+// 16(w%4).. and dims 64(w/4)..; the dk block for keys 16(w%4).. and dims
+// 64(w/4)..
 constexpr int kBW = 8;              // waves per workgroup (MFMA path)
 constexpr int kBT8 = kBW * 64;
 
