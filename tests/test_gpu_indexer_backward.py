@@ -10,8 +10,9 @@ tiles, -1 entries anywhere (in any order) and an empty row; two chunk calls
 adding into one dk; the fp32 path for other shapes; sampled rows of the last
 chunk of the 128K prefill (with the gradient zero outside the sampled rows, so
 that dk is known exactly); and a sequence longer than the two-pass
-reduction's 4096-row scan window.  Every sparse MFMA case runs with dk by
-atomics and with the two-pass dk (a workspace given)."""
+reduction's 4096-row scan window, the first chunk (key blocks split over
+workgroups) and keys shared by every row.  Every sparse MFMA case runs with
+dk by atomics and with the two-pass dk (a workspace given)."""
 import numpy as np
 import pytest
 import torch
@@ -284,6 +285,43 @@ def test_backward_two_pass_first_chunk_split_blocks():
     dq, dw, dk = _backward(prob, sub, grad.to(DEV), idx, two_pass=True)
     _check(sub, prob, rows, rows, [0] * len(rows), grad, idx, dq, dw, dk)
     full = (torch.randn(C, wl.topk, generator=gen) * 1e-3).to(DEV)
+    _, _, dk_a = _backward(prob, sub, full, idx)
+    _, _, dk_t = _backward(prob, sub, full, idx, two_pass=True)
+    scale = dk_a.abs().max().item()
+    assert scale > 0
+    assert (dk_t - dk_a).abs().max().item() <= 1e-5 * scale
+
+
+def test_backward_two_pass_keys_shared_by_every_row():
+    """Every row of the last 128K chunk selects keys 0..63 (plus 1984 random
+    causal keys, ascending): the first 64-key block then holds 4096 x 64
+    pairs, 64 of the reduction's 4096-pair batches, and each of those keys'
+    runs spans several half-waves.  Sampled rows carry the gradient (dk is
+    exactly theirs, against the oracle); with the gradient on every row the
+    two-pass dk agrees with the atomic one to fp32 summation order."""
+    wl = wk.CHUNKED_PREFILL_128K
+    _announce("indexer backward two-pass, keys 0..63 shared by every row")
+    inp = wk.generate(wl, device=DEV)
+    L, C, k = wl.seq_len, wl.chunk, wl.topk
+    r0 = L - C
+    sl = slice(r0, L)
+    prob = dsa.Problem.from_workload(wl, inp, device=DEV, q_rows=sl, q_pos0=r0)
+    sub = dict(inp)
+    for key in ("q_fp8", "q_scale", "w", "q"):
+        sub[key] = inp[key][sl]
+    rng = np.random.default_rng(31)
+    idx_np = np.empty((C, k), dtype=np.int32)
+    idx_np[:, :64] = np.arange(64)
+    for i in range(C):
+        idx_np[i, 64:] = np.sort(rng.choice(np.arange(64, r0 + i + 1), size=k - 64, replace=False))
+    idx = torch.as_tensor(idx_np, device=DEV)
+    rows = [0, 777, 2048, 4095]
+    gen = torch.Generator(device="cpu").manual_seed(33)
+    grad = torch.zeros(C, k)
+    grad[rows] = torch.randn(len(rows), k, generator=gen) * 1e-3
+    dq, dw, dk = _backward(prob, sub, grad.to(DEV), idx, two_pass=True)
+    _check(sub, prob, rows, [r0 + r for r in rows], [0] * len(rows), grad, idx, dq, dw, dk)
+    full = (torch.randn(C, k, generator=gen) * 1e-3).to(DEV)
     _, _, dk_a = _backward(prob, sub, full, idx)
     _, _, dk_t = _backward(prob, sub, full, idx, two_pass=True)
     scale = dk_a.abs().max().item()
