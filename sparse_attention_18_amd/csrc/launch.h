@@ -161,17 +161,21 @@ __device__ __forceinline__ int64_t row_pos(const SeqInfo &s, int64_t r) {
 // Sequence owning packed query row r: the last b with q_offsets[b] <= r
 // (offsets are non-decreasing, so that is the count of such b, minus one).
 // r must be uniform across the wave and every lane active: each lane loads
-// offsets lane, lane + 64, ... at once and a ballot counts them, which costs
-// one memory round trip instead of the log2(batch) dependent loads of a
-// binary search.
+// offsets lane, lane + 64, lane + 128 and lane + 192 at once and ballots count
+// them, which costs one memory round trip per 256 sequences instead of the
+// log2(batch) dependent loads of a binary search.
 __device__ __forceinline__ int find_seq(const SeqLayout &L, int64_t r) {
   const int lane = __lane_id();
   int cnt = 0;
-#pragma unroll 4
-  for (int base = 0; base < L.batch; base += 64) {
-    const int i = base + lane;
-    const bool le = i < L.batch && (int64_t)L.q_offsets[i] <= r;
-    cnt += __popcll(__ballot(le));
+  for (int base = 0; base < L.batch; base += 256) {
+    bool le[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = base + 64 * u + lane;
+      le[u] = i < L.batch && (int64_t)L.q_offsets[i] <= r;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) cnt += __popcll(__ballot(le[u]));
   }
   return cnt > 0 ? cnt - 1 : 0;
 }
