@@ -33,7 +33,7 @@ What it computes, stage by stage, in the order the pages give:
    of the indexer scores), with its gradient taken with respect to the scores,
    and that gradient carried back through the indexer to q, w and k.
 
-Readings where the pages are silent or garbled (each listed in the design doc):
+Readings where the pages are silent or garbled:
 the indexer formula and FP8 format; causality (a key is visible iff its
 position <= the query's); the skillmd pseudo-code applies softmax to the
 indexer scores, whereas the ivugangingo article runs a separate MQA/MLA path
