@@ -117,8 +117,8 @@ def test_backward_dense_mfma():
 
 @TWO_PASS
 def test_backward_custom_indices_gaps_and_empty_row(two_pass):
-    """Indices in random order (the two-pass form sorts them), k = 80 (not a
-    multiple of the 64-key tile)."""
+    """Indices in random order (the two-pass form sorts them), a few keys
+    listed twice in a row, k = 80 (not a multiple of the 64-key tile)."""
     wl = MED.scaled(seq_len=400, topk=80)
     _announce(f"indexer backward sparse, -1 anywhere, empty row, two_pass={two_pass}")
     inp = wk.generate(wl)
@@ -131,6 +131,11 @@ def test_backward_custom_indices_gaps_and_empty_row(two_pass):
         m = min(r + 1, int(rng.integers(1, k + 1)))
         idx_np[r, rng.choice(k, size=m, replace=False)] = rng.choice(r + 1, size=m, replace=False)
     idx_np[5] = -1
+    # a key listed twice in a row counts once per entry
+    for r in (9, 150, 399):
+        v = np.flatnonzero(idx_np[r] >= 0)
+        assert len(v) >= 2
+        idx_np[r, v[1]] = idx_np[r, v[0]]
     idx = torch.as_tensor(idx_np, device=DEV)
     grad = torch.as_tensor(rng.standard_normal((L, k)) * 1e-3, dtype=torch.float32, device=DEV)
     dq, dw, dk = _backward(prob, g, grad, idx, two_pass=two_pass)
