@@ -247,7 +247,8 @@ dsa_status dsa_indexer_align_loss(const dsa_problem *p, const uint16_t *q, const
  * continues": the indexer is what that loss trains).  With q~ = q_scale * q8
  * and k~ = k_scale * k8 the dequantised values, z[j, s] = q~[r, j] . k~[s],
  * and G[r, s] the given gradient over row r's keys K_r (dense: positions
- * 0..pos(r); sparse: the valid entries of topk_idx[r]):
+ * 0..pos(r); sparse: the valid entries of topk_idx[r], a key listed twice
+ * counting twice, in any order):
  *   dw[r, j]     = sum_{s in K_r} G[r, s] * ReLU(z[j, s])
  *   dq[r, j, :]  = sum_{s in K_r} G[r, s] * w[r, j] * [z[j, s] > 0] * k~[s, :]
  *   dk[b, s, :] += sum_{r of b} sum_j G[r, s] * w[r, j] * [z[j, s] > 0] * q~[r, j, :]
