@@ -87,8 +87,18 @@ enum { DSA_WS_TOPK = 0, DSA_WS_ATTN = 1, DSA_WS_FORWARD = 2, DSA_WS_INDEXER_BWD 
  *       sum_{j < H_I} w[r*H_I + j] * max(0, sum_{d < d_I} q8[r,j,d] * k8[s',d])
  * for every query row r and every position s <= pos(r), where s' is the
  * packed key row kv_offsets[b] + s and q8/k8 are the decoded e4m3fn values.
- * Entries with s > pos(r) are left untouched.  Products are exact in fp32;
- * accumulation is fp32.
+ * Entries with s > pos(r) are left untouched.  The scales must be >= 0 (they
+ * are applied outside the ReLU; a zero scale gives zero scores).
+ * Arithmetic: every e4m3 x e4m3 product is exact in fp32 and the dot products
+ * and the head sum accumulate in fp32.  Batches with more than two query rows
+ * per sequence take the prefill kernel, which evaluates the head sum as
+ *   sum_j (w_j/2) |x_j|  +  Qe . k8,     Qe[d] = sum_j (w_j/2) q8[r,j,d]
+ * (ReLU(x) = (x + |x|)/2) with Qe carried as three e4m3 pieces: that term
+ * errs by up to about 2^-12 * max_d |Qe[d]| * sum_d |k8[s',d]| (times the
+ * scales).  A score that is exactly 0 (every dot product <= 0) can therefore
+ * come out as a tiny value of either sign, and the prefill and decode (at
+ * most two query rows per sequence) kernels can return slightly different
+ * scores, and so a different selection at a near-tie, for the same pair.
  *   q_fp8   [total_q, H_I, d_I] uint8   q_scale [total_q] float
  *   w       [total_q, H_I] float        k_fp8   [total_kv, d_I] uint8
  *   k_scale [total_kv] float            scores  [total_q, ld_scores] float
@@ -252,7 +262,9 @@ dsa_status dsa_indexer_align_loss(const dsa_problem *p, const uint16_t *q, const
  *   dw[r, j]     = sum_{s in K_r} G[r, s] * ReLU(z[j, s])
  *   dq[r, j, :]  = sum_{s in K_r} G[r, s] * w[r, j] * [z[j, s] > 0] * k~[s, :]
  *   dk[b, s, :] += sum_{r of b} sum_j G[r, s] * w[r, j] * [z[j, s] > 0] * q~[r, j, :]
- * (the ReLU's derivative at 0 is taken as 0).  dq and dw are gradients with
+ * (the ReLU's derivative at 0 is taken as 0, so a row or key whose scale is
+ * 0 -- scales are >= 0 as for dsa_indexer_scores -- has z = 0 and passes no
+ * gradient through the mask).  dq and dw are gradients with
  * respect to the dequantised q~ and w and are overwritten; dk, with respect
  * to k~, is ADDED to (a key is shared by many rows and, in a chunked
  * prefill, by several calls), in an order that varies from run to run, so

@@ -361,6 +361,8 @@ dsa_status attn_impl(const dsa_problem *p, const dsa_paged_kv *pg, const uint16_
   const size_t need = ws_attn(p);
   DSA_CHECK(workspace_bytes >= need && (need == 0 || workspace != nullptr), DSA_ERR_WORKSPACE,
             "attention workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  DSA_CHECK(need == 0 || aligned16(workspace), DSA_ERR_INVALID_ARGUMENT,
+            "workspace must be 16-byte aligned");
   return hip_status(dsa::launch_sparse_attn(attn_args(p, q, kv, topk_idx, out, lse, workspace,
                                                       workspace_bytes, pg),
                                             static_cast<hipStream_t>(stream)),
@@ -565,3 +567,4 @@ dsa_status dsa_indexer_backward(const dsa_problem *p, const uint8_t *q_fp8, cons
 }
 
 }  // extern "C"
+

@@ -336,7 +336,8 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs p) {
 
   // Keys and key scales are read through buffer descriptors spanning this
   // wave's slice: loads past it return zeros, so every load is issued
-  // unconditionally.  With no branch around them the compiler counts them,
+  // unconditionally.  The whole offset goes in the vector offset (the scalar
+  // offset is not part of the range check).  With no branch around them the compiler counts them,
   // and the wait before a step's MFMAs covers only that step's loads; the
   // next step's stay in flight.  Dims at or past d_I get an offset past the
   // range (zeros too).  The scores go to LDS and are written out after the
@@ -363,9 +364,9 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs p) {
       const __amdgpu_buffer_rsrc_t sst = rsrc(p.k_scale + rb, cnt * 4);
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const int so = kb * 16 * d;
-        const v4i lo = __builtin_amdgcn_raw_buffer_load_b128(kst, koff, so, 0);
-        const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(kst, koff + 16, so, 0);
+        const int vo = koff + kb * 16 * d;
+        const v4i lo = __builtin_amdgcn_raw_buffer_load_b128(kst, vo, 0, 0);
+        const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(kst, vo + 16, 0, 0);
         kr[kb] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
       ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sst, lane * 4, 0, 0));
@@ -373,12 +374,12 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs p) {
     }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-      const int so = (st * 64 + kb * 16) * d;
-      const v4i lo = __builtin_amdgcn_raw_buffer_load_b128(krs, koff, so, 0);
-      const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(krs, koff + 16, so, 0);
+      const int vo = koff + (st * 64 + kb * 16) * d;
+      const v4i lo = __builtin_amdgcn_raw_buffer_load_b128(krs, vo, 0, 0);
+      const v4i hi = __builtin_amdgcn_raw_buffer_load_b128(krs, vo + 16, 0, 0);
       kr[kb] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
-    ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, lane * 4, st * 256, 0));
+    ks = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, lane * 4 + st * 256, 0, 0));
   };
   auto score_step = [&](int st, const v8i (&kr)[4], float ks) {
     float part[4];

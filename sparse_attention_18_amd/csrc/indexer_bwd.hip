@@ -329,6 +329,10 @@ __global__ __launch_bounds__(kBT8) void indexer_bwd_kernel(IndexerBwdArgs p) {
     }
     const float gk = tg[buf][key_l] * tks[buf][key_l];   // g * k_scale of the lane's key
     const float cw = gk * qsc;
+    // The mask is decided on the e4m3 dot product, which has the sign of z
+    // only when both scales are positive; with a zero scale z is 0 and the
+    // ReLU's derivative there is 0.
+    const bool sc_pos = qsc > 0.f && tks[buf][key_l] > 0.f;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int hb = 2 * wh + i;
@@ -337,7 +341,7 @@ __global__ __launch_bounds__(kBT8) void indexer_bwd_kernel(IndexerBwdArgs p) {
       for (int j = 0; j < 4; ++j) {
         const float zr = z[i][j];
         dw[i][j] = fmaf(fmaxf(zr, 0.f), cw, dw[i][j]);
-        const float e = zr > 0.f ? wv[i][j] * gk : 0.f;
+        const float e = (zr > 0.f && sc_pos) ? wv[i][j] * gk : 0.f;
         // hi = e rounded to bf16 (round to nearest even), lo = the remainder
         const __bf16 eh16 = (__bf16)e;
         const __bf16 el16 = (__bf16)(e - (float)eh16);
@@ -386,7 +390,9 @@ __global__ __launch_bounds__(kBT8) void indexer_bwd_kernel(IndexerBwdArgs p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int key = 16 * w4 + 4 * g4 + j;
-      const float f = qsc / tks[buf][key];
+      // E already carries k_scale; a zero scale has E = 0 and a zero factor
+      const float kscl = tks[buf][key];
+      const float f = kscl > 0.f ? qsc / kscl : 0.f;
       if constexpr (kStore) {
         // the key's rank t0 + key < kpad (a multiple of 64 >= k); ranks past
         // m get zeros, which the reduction never reads

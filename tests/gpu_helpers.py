@@ -103,14 +103,43 @@ def check_attention_rows(out, lse, q, kv, idx, rows, kv0s, scale, d_latent):
     ref = np.stack(refs)
     max_abs = np.abs(o_gpu - ref).max()
     rel_f = np.linalg.norm(o_gpu - ref) / max(np.linalg.norm(ref), 1e-30)
+    beyond, row_ulps = bf16_rounding_split(o_gpu, ref)
     assert max_abs <= ATTN_MAX_ABS and rel_f <= ATTN_REL_F, \
-        f"attention max-abs {max_abs:.3e} relF {rel_f:.3e}"
+        (f"attention max-abs {max_abs:.3e} relF {rel_f:.3e} ({beyond:.3e} beyond the bf16 output "
+         f"rounding; worst row {row_ulps:.2f} half-ulps of its largest value)")
     if l_gpu is not None:
         lref = np.stack(lrefs)
         fin = np.isfinite(lref)
         assert (np.isfinite(l_gpu) == fin).all()
         assert np.abs(l_gpu[fin] - lref[fin]).max() <= 1e-3 * max(1.0, np.abs(lref[fin]).max())
+    check_attention_rows.last_rounding_split = (beyond, row_ulps)
     return max_abs, rel_f
+
+
+def _bf16_half_ulp(x):
+    mag = np.maximum(np.abs(x), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(mag)) - 8)
+
+
+def bf16_rounding_split(got, ref):
+    """How much of the attention error is the bf16 output rounding.
+
+    The output is an fp32 result rounded to nearest bf16, which alone moves
+    an element by up to half a bf16 ulp of its value.  Returns
+    (beyond, row_ulps): ``beyond`` = max over elements of
+    max(0, |got - ref| - half ulp), the error left after the rounding
+    (near 0 when rounding explains everything); ``row_ulps`` = max over rows
+    (leading index) of the row's worst |got - ref| in half ulps of the row's
+    largest |ref| (rounding alone gives at most 1)."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.abs(got - ref)
+    half = np.maximum(_bf16_half_ulp(ref), _bf16_half_ulp(got))
+    beyond = float(np.maximum(err - half, 0.0).max()) if err.size else 0.0
+    e2 = err.reshape(err.shape[0], -1)
+    r2 = np.abs(ref).reshape(ref.shape[0], -1)
+    row_ulps = float((e2.max(axis=1) / _bf16_half_ulp(r2.max(axis=1))).max()) if err.size else 0.0
+    return beyond, row_ulps
 
 
 

@@ -203,6 +203,21 @@ def test_paged_attention_lifts_the_packed_row_bound():
     assert "topk_idx" in _msg()
 
 
+def test_attention_split_workspace_must_be_aligned():
+    """A few-token batch splits each token's rows over several workgroups,
+    whose vector partial results go to the workspace: it must be 16-byte
+    aligned like every other device pointer."""
+    lib = binding.load_library()
+    p = _problem(batch=64, total_q=64, max_q_len=1, total_kv=64 * 9000, max_kv_len=9000)
+    need = lib.dsa_workspace_bytes(ctypes.byref(p), binding.WS_ATTN)
+    assert need > 0
+    assert lib.dsa_sparse_attn(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE + 8, need,
+                               None) == binding.DSA_ERR_INVALID_ARGUMENT
+    assert "aligned" in _msg()
+    assert lib.dsa_sparse_attn(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, FAKE, need - 1,
+                               None) == binding.DSA_ERR_WORKSPACE
+
+
 def _align(p, lse=FAKE, scores=FAKE, idx=FAKE, loss=FAKE, grad=FAKE, ld=4096, ld_grad=2048):
     lib = binding.load_library()
     return lib.dsa_indexer_align_loss(ctypes.byref(p), FAKE, FAKE, lse, scores, ld, idx, loss, grad,

@@ -143,6 +143,38 @@ def test_backward_custom_indices_gaps_and_empty_row(two_pass):
     assert not dq[5].any() and not dw[5].any()
 
 
+@pytest.mark.parametrize("form", ["atomic", "two_pass", "dense"])
+def test_backward_zero_scales_and_zero_key(form):
+    """Zero scales dequantise to zero vectors: z = 0 there, the ReLU's
+    derivative is 0, and the gradients must be finite and match the oracle
+    (a key whose scale is 0 but whose e4m3 bytes are not, a key whose bytes
+    are all zero, and query rows whose scale is 0)."""
+    wl = MED.scaled(seq_len=320)
+    _announce(f"indexer backward, zero scales and a zero key row, {form}")
+    inp = wk.generate(wl)
+    for key in (0, 3, 40, 200, 319):
+        inp["k_scale"][key] = 0.0
+    inp["k_fp8"][77] = 0
+    for row in (2, 150, 300):
+        inp["q_scale"][row] = 0.0
+    prob = dsa.Problem.from_workload(wl, inp)
+    g = H.to_dev(inp)
+    L = wl.seq_len
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    if form == "dense":
+        ld = prob.ld_scores()
+        grad = (torch.randn(L, ld, generator=gen) * 1e-3).to(DEV)
+        idx = None
+    else:
+        _, idx = _topk(prob, g)
+        grad = (torch.randn(L, wl.topk, generator=gen) * 1e-3).to(DEV)
+    dq, dw, dk = _backward(prob, g, grad, idx, two_pass=form == "two_pass")
+    for name, t in (("dq", dq), ("dw", dw), ("dk", dk)):
+        assert torch.isfinite(t).all(), f"{name} has non-finite entries"
+    _check(inp, prob, list(range(L)), list(range(L)), [0] * L, grad, idx, dq, dw, dk)
+    assert not dq[[2, 150, 300]].any(), "a zero query scale gives dq = 0"
+
+
 @TWO_PASS
 def test_backward_chunks_add_into_one_dk(two_pass):
     """Two chunk calls (rows [0, 300) and [300, 600)) adding into one dk give
