@@ -298,6 +298,30 @@ dsa_status dsa_indexer_backward(const dsa_problem *p, const uint8_t *q_fp8, cons
                                 float *dq, float *dw, float *dk, void *workspace,
                                 size_t workspace_bytes, void *stream);
 
+/*
+ * dsa_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops that must not
+ * call hipMalloc, harnesses that forbid it).  The workspace dsa_forward
+ * would take is a fixed device array of DSA_NOALLOC_SCRATCH_BYTES inside the
+ * library instead: one per GPU, created when the library's code is first
+ * loaded on that GPU and held until the process ends.  The call itself
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ * Arguments and results as for dsa_forward, on the current device (stream
+ * must belong to it).  Problems whose dsa_workspace_bytes(p, DSA_WS_FORWARD)
+ * exceeds DSA_NOALLOC_SCRATCH_BYTES are refused with DSA_ERR_UNSUPPORTED
+ * before anything is enqueued (the decode batch of 64 sequences at 128K
+ * context and prefills of a few thousand tokens fit).  Every call on a GPU
+ * shares that GPU's array, whose contents need no initialisation and are
+ * left as the last call wrote them: calls that overlap in time on one GPU
+ * (different streams or host threads without ordering between them) race
+ * on it and give wrong results.
+ */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+dsa_status dsa_forward_noalloc(const dsa_problem *p, const uint8_t *q_fp8, const float *q_scale,
+                               const float *w, const uint8_t *k_fp8, const float *k_scale,
+                               const uint16_t *q, const uint16_t *kv, uint16_t *out, float *lse,
+                               int32_t *topk_idx_out, void *stream);
+
 /* Bytes of device workspace the given entry point needs for problem p
  * (which = DSA_WS_TOPK, DSA_WS_ATTN, DSA_WS_FORWARD, or DSA_WS_INDEXER_BWD
  * for the two-pass form of dsa_indexer_backward); 0 if none.  Returns

@@ -27,7 +27,9 @@ WS_TOPK, WS_ATTN, WS_FORWARD, WS_INDEXER_BWD = 0, 1, 2, 3
 
 EXPORTED = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward",
             "dsa_indexer_scores_paged", "dsa_sparse_attn_paged", "dsa_forward_paged",
-            "dsa_indexer_align_loss", "dsa_indexer_backward", "dsa_workspace_bytes", "dsa_last_error", "dsa_version")
+            "dsa_indexer_align_loss", "dsa_indexer_backward", "dsa_workspace_bytes", "dsa_last_error", "dsa_version",
+            "dsa_forward_noalloc")
+NOALLOC_SCRATCH_BYTES = 256 << 20      # DSA_NOALLOC_SCRATCH_BYTES in include/dsa.h
 
 
 class DsaLibraryError(RuntimeError):
@@ -104,9 +106,10 @@ def load_library():
         lib.dsa_forward_paged.argtypes = [P, G, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         lib.dsa_indexer_align_loss.argtypes = [P, vp, vp, vp, vp, i64, vp, vp, vp, i64, vp]
         lib.dsa_indexer_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]
+        lib.dsa_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward",
                      "dsa_indexer_scores_paged", "dsa_sparse_attn_paged", "dsa_forward_paged",
-                     "dsa_indexer_align_loss", "dsa_indexer_backward"):
+                     "dsa_indexer_align_loss", "dsa_indexer_backward", "dsa_forward_noalloc"):
             getattr(lib, name).restype = ctypes.c_int
         lib.dsa_workspace_bytes.argtypes = [P, ctypes.c_int]
         lib.dsa_workspace_bytes.restype = sz
@@ -277,6 +280,27 @@ def forward(prob: Problem, q_fp8, q_scale, w, k_fp8, k_scale, q, kv, out, lse=No
         _ptr(lse, torch.float32, "lse", (c.total_q, c.heads)),
         _ptr(idx_out, torch.int32, "idx_out", (c.total_q, c.topk)),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
+
+
+def forward_noalloc(prob: Problem, q_fp8, q_scale, w, k_fp8, k_scale, q, kv, out, lse=None,
+                    idx_out=None, stream=None):
+    """dsa_forward_noalloc: dsa_forward with the library's own device scratch as
+    its workspace (no allocation in the call; problems whose forward
+    workspace exceeds NOALLOC_SCRATCH_BYTES are refused)."""
+    c = prob.c
+    D = c.d_latent + c.d_rope
+    _check(load_library().dsa_forward_noalloc(
+        ctypes.byref(c),
+        _ptr(q_fp8, torch.uint8, "q_fp8", (c.total_q, c.idx_heads, c.idx_dim)),
+        _ptr(q_scale, torch.float32, "q_scale", (c.total_q,)),
+        _ptr(w, torch.float32, "w", (c.total_q, c.idx_heads)),
+        _ptr(k_fp8, torch.uint8, "k_fp8", (c.total_kv, c.idx_dim)),
+        _ptr(k_scale, torch.float32, "k_scale", (c.total_kv,)),
+        _ptr(q, torch.bfloat16, "q", (c.total_q, c.heads, D)),
+        _ptr(kv, torch.bfloat16, "kv", (c.total_kv, D)),
+        _ptr(out, torch.bfloat16, "out", (c.total_q, c.heads, c.d_latent)),
+        _ptr(lse, torch.float32, "lse", (c.total_q, c.heads)),
+        _ptr(idx_out, torch.int32, "idx_out", (c.total_q, c.topk)), _stream(stream)))
 
 
 def indexer_align_loss(prob: Problem, q, kv, lse, scores, loss, grad, idx=None, ld=None,

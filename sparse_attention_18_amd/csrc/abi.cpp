@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/dsa.h"
@@ -568,3 +569,59 @@ dsa_status dsa_indexer_backward(const dsa_problem *p, const uint8_t *q_fp8, cons
 
 }  // extern "C"
 
+// ---------------------------------------------------------------------------
+// dsa_forward_noalloc: dsa_forward with its workspace in a fixed device array
+// of this library, for callers that cannot allocate device memory.
+
+namespace {
+
+// One copy per GPU, made when the library's code object is loaded on that
+// device and held until the process ends.  In host code this name is only a
+// stand-in for the symbol: its device address comes from hipGetSymbolAddress
+// (scratch_address below), and only that address is ever passed on.
+static __device__ __align__(256) uint8_t scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device (the first call on it) and kept.
+dsa_status scratch_address(void **out) {
+  int dev = -1;
+  DSA_TRY(hip_status(hipGetDevice(&dev), "hipGetDevice"));
+  DSA_CHECK(dev >= 0 && dev < kMaxDevices, DSA_ERR_UNSUPPORTED,
+            "device %d is beyond the %d devices dsa_forward_noalloc tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *ptr = nullptr;
+    DSA_TRY(hip_status(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)"));
+    DSA_CHECK(ptr != nullptr && aligned16(ptr), DSA_ERR_HIP, "scratch has no usable device address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+dsa_status dsa_forward_noalloc(const dsa_problem *p, const uint8_t *q_fp8, const float *q_scale,
+                               const float *w, const uint8_t *k_fp8, const float *k_scale,
+                               const uint16_t *q, const uint16_t *kv, uint16_t *out, float *lse,
+                               int32_t *topk_idx_out, void *stream) {
+  // Sizes first, so that an oversized problem is refused before any HIP call.
+  DSA_TRY(check_problem(p));
+  const size_t need = forward_ws(p).total;
+  DSA_CHECK(need <= (size_t)DSA_NOALLOC_SCRATCH_BYTES, DSA_ERR_UNSUPPORTED,
+            "dsa_forward_noalloc: this problem needs %zu bytes of workspace, more than the "
+            "%zu-byte device scratch; use dsa_forward with a caller workspace",
+            need, (size_t)DSA_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  DSA_TRY(scratch_address(&ws));
+  return forward_impl(p, nullptr, q_fp8, q_scale, w, k_fp8, k_scale, q, kv, out, lse, topk_idx_out,
+                      ws, (size_t)DSA_NOALLOC_SCRATCH_BYTES, stream);
+}
+
+}  // extern "C"

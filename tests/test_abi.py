@@ -218,6 +218,24 @@ def test_attention_split_workspace_must_be_aligned():
                                None) == binding.DSA_ERR_WORKSPACE
 
 
+def test_forward_noalloc_refuses_problems_beyond_its_scratch():
+    """Sizes are checked before any HIP call: a 4096-row chunk of a 128K
+    prefill needs a 2 GB scores matrix, far beyond the fixed scratch."""
+    lib = binding.load_library()
+    n = 131072
+    p = _problem(total_kv=n, max_kv_len=n)
+    need = lib.dsa_workspace_bytes(ctypes.byref(p), binding.WS_FORWARD)
+    assert need > binding.NOALLOC_SCRATCH_BYTES
+    assert lib.dsa_forward_noalloc(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   None, None, None) == binding.DSA_ERR_UNSUPPORTED
+    assert "scratch" in _msg() and str(need) in _msg()
+    assert lib.dsa_forward_noalloc(None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                   None, None, None) == binding.DSA_ERR_INVALID_ARGUMENT
+    # the 64-sequence decode batch at 128K context fits
+    dec = _problem(batch=64, total_q=64, max_q_len=1, total_kv=64 * n, max_kv_len=n)
+    assert lib.dsa_workspace_bytes(ctypes.byref(dec), binding.WS_FORWARD) <= binding.NOALLOC_SCRATCH_BYTES
+
+
 def _align(p, lse=FAKE, scores=FAKE, idx=FAKE, loss=FAKE, grad=FAKE, ld=4096, ld_grad=2048):
     lib = binding.load_library()
     return lib.dsa_indexer_align_loss(ctypes.byref(p), FAKE, FAKE, lse, scores, ld, idx, loss, grad,
