@@ -20,9 +20,20 @@ published peaks (HBM 8 TB/s, dense FP8 5.0 PFLOP/s, dense bf16 2.5 PFLOP/s).
 ``cpu_baseline`` is the float64 oracle on a bounded sample of query rows of
 the same workload, on the host's cores.
 
+The 4K and 32K prefills (one sequence each, every token a query against its
+causal prefix) are timed stage by stage as ``prefill_configs``, with a 1 GiB
+read between iterations so that no input is left in the 256 MB MALL; the
+decode step is also timed stage by stage (``decode_stages``) and with the
+same flush between steps.  ``measured_peaks`` are what the box reaches on
+plain work (a device copy, a read-only reduction, large hipBLASLt GEMMs in
+bf16 and fp8), and every stage fraction is also given against them
+(``frac_measured``).  ``cpu_baseline_configs`` runs the oracle over every row
+of the tiny prefill, the 4K prefill and the decode batch, and
+``cpu_baseline_single_thread`` a small sample with one BLAS thread.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode]
                        [--no-train] [--no-cpu-baseline] [--cpu-rows R]
-                       [--stages-json PATH]
+                       [--no-small-prefill] [--only PART] [--stages-json PATH]
 """
 from __future__ import annotations
 
@@ -134,6 +145,93 @@ def align_flops(wl, positions):
     return float(m.sum()) * 2.0 * wl.heads * wl.d_qk
 
 
+def indexer_decode_bytes(wl, positions):
+    """Decode indexer (HBM-bound): per cached key its FP8 row and scale read
+    once and its fp32 score written (d_I + 4 + 4 B)."""
+    n = np.asarray(positions, dtype=np.float64) + 1
+    return float(n.sum()) * (wl.idx_dim + 8)
+
+
+# ----------------------------------------------------------------- measured peaks
+def _median_seconds(fn, n=10, warm=3):
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(n):
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    return float(np.median(ts)) * 1e-3
+
+
+def measured_peaks(dev):
+    """What this machine reaches on plain work: a 2 GiB device copy (read + write
+    bytes), a read-only reduction over it, and 8192^3 GEMMs through torch
+    (hipBLASLt) in bf16 and fp8 e4m3.  Context for the spec peaks, not a
+    replacement: each stage fraction is reported against both."""
+    res = {}
+    src = torch.ones(1 << 29, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    nbytes = src.numel() * 4
+    res["hbm_copy_GBps"] = round(2 * nbytes / _median_seconds(lambda: dst.copy_(src)) / 1e9, 1)
+    res["hbm_read_GBps"] = round(nbytes / _median_seconds(lambda: src.sum()) / 1e9, 1)
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    res["bf16_gemm_TFLOPs"] = round(2 * n ** 3 / _median_seconds(lambda: torch.mm(a, b)) / 1e12, 1)
+    try:
+        a8 = a.to(torch.float8_e4m3fn)
+        b8 = b.to(torch.float8_e4m3fn).t()          # column-major right operand
+        one = torch.ones((), device=dev)
+        t = _median_seconds(lambda: torch._scaled_mm(a8, b8, scale_a=one, scale_b=one,
+                                                     out_dtype=torch.bfloat16))
+        res["fp8_gemm_TFLOPs"] = round(2 * n ** 3 / t / 1e12, 1)
+    except Exception as e:  # pragma: no cover - depends on the torch build
+        log(f"[bench] fp8 GEMM probe unavailable: {e}")
+        res["fp8_gemm_TFLOPs"] = None
+    res["how"] = ("2 GiB torch copy_ (read + write bytes) and sum (read bytes); 8192^3 torch.mm "
+                  "(bf16) and torch._scaled_mm (fp8 e4m3, bf16 out); medians of 10")
+    return res
+
+
+_SPEC = {"hbm": (HBM_PEAK, "GB/s", 1e9), "mfma": (FP8_PEAK, "TFLOP/s", 1e12)}
+
+
+def _measured_peak(bound, peaks):
+    if not peaks:
+        return None
+    if bound == "hbm":
+        return max(peaks["hbm_copy_GBps"], peaks["hbm_read_GBps"]) * 1e9
+    v = peaks.get("fp8_gemm_TFLOPs")
+    return v * 1e12 if v else None
+
+
+def stage_entry(ms, launches, bound, amount, peaks=None, bf16_flops=None):
+    """One stage's record: time, algorithmic rate, and its fraction of the spec
+    peak (``frac``) and of the box's measured peak (``frac_measured``)."""
+    peak, unit, scale = _SPEC[bound]
+    t = ms * 1e-3
+    rate = amount / t
+    e = {"ms_per_step": round(ms, 4), "launches_per_step": launches,
+         "avg_launch_us": round(ms / launches * 1e3, 1), "bound": bound,
+         "achieved": round(rate / scale, 1), "peak": round(peak / scale, 1), "unit": unit,
+         "frac": round(rate / peak, 4)}
+    mp = _measured_peak(bound, peaks)
+    if mp:
+        e["frac_measured"] = round(rate / mp, 4)
+    if bf16_flops is not None:
+        e["bf16_tflops"] = round(bf16_flops / t / 1e12, 1)
+        e["bf16_mfma_frac"] = round(bf16_flops / t / BF16_PEAK, 4)
+        if peaks and peaks.get("bf16_gemm_TFLOPs"):
+            e["bf16_frac_measured"] = round(bf16_flops / t / (peaks["bf16_gemm_TFLOPs"] * 1e12), 4)
+    return e
+
+
 # ----------------------------------------------------------------- prefill step
 class ChunkedPrefill:
     def __init__(self, wl, dev):
@@ -213,7 +311,7 @@ class ChunkedPrefill:
                 events[ci][2].record()
 
 
-def run_prefill(args, dev):
+def run_prefill(args, dev, peaks=None):
     wl = wk.CHUNKED_PREFILL_128K
     bench = ChunkedPrefill(wl, dev)
     for i in range(args.warmup):
@@ -246,36 +344,78 @@ def run_prefill(args, dev):
     stage_ms /= args.steps
     per_chunk /= args.steps
     pos = bench.positions
-    work = {
-        "indexer": {"bound": "mfma", "amount": indexer_flops(wl, pos), "peak": FP8_PEAK,
-                    "unit": "TFLOP/s", "scale": 1e12, "dtype": "fp8"},
-        "topk": {"bound": "hbm", "amount": topk_bytes(wl, pos), "peak": HBM_PEAK,
-                 "unit": "GB/s", "scale": 1e9},
-        "sparse_attn": {"bound": "hbm", "amount": attn_bytes(wl, pos), "peak": HBM_PEAK,
-                        "unit": "GB/s", "scale": 1e9,
-                        "flops": attn_flops(wl, pos)},
+    stages = {
+        "indexer": stage_entry(stage_ms[0], nch, "mfma", indexer_flops(wl, pos), peaks),
+        "topk": stage_entry(stage_ms[1], nch, "hbm", topk_bytes(wl, pos), peaks),
+        "sparse_attn": stage_entry(stage_ms[2], nch, "hbm", attn_bytes(wl, pos), peaks,
+                                   bf16_flops=attn_flops(wl, pos)),
     }
-    stages = {}
-    for j, name in enumerate(("indexer", "topk", "sparse_attn")):
-        w = work[name]
-        t = stage_ms[j] * 1e-3
-        rate = w["amount"] / t
-        stages[name] = {
-            "ms_per_step": round(stage_ms[j], 3),
-            "launches_per_step": nch,
-            "avg_launch_us": round(stage_ms[j] / nch * 1e3, 1),
-            "bound": w["bound"],
-            "achieved": round(rate / w["scale"], 1),
-            "peak": round(w["peak"] / w["scale"], 1),
-            "unit": w["unit"],
-            "frac": round(rate / w["peak"], 4),
-        }
-        if "flops" in w:
-            stages[name]["bf16_tflops"] = round(w["flops"] / t / 1e12, 1)
-            stages[name]["bf16_mfma_frac"] = round(w["flops"] / t / BF16_PEAK, 4)
     ms_per_step = gpu_ms / args.steps
     value = wl.seq_len / (ms_per_step * 1e-3)
     return bench, wl, value, ms_per_step, stages, per_chunk
+
+
+class MallFlush:
+    """A 1 GiB buffer read between timed iterations: four times the 256 MB
+    MALL, so no input of the previous iteration is still cached there.  A
+    read, not a write: written lines would be written back to HBM while the
+    next timed kernel runs, and that kernel would pay for them."""
+
+    def __init__(self, dev):
+        self.buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        torch.sum(self.buf)
+
+
+def run_prefill_single(wl, dev, flush, peaks=None, iters=10, warmup=2):
+    """One prefill sequence, every token a query against its causal prefix:
+    indexer, top-k and attention through the three stage calls, each stage
+    bracketed by events, the MALL flushed before every iteration.  Returns
+    the medians over the iterations and the inputs (for the CPU baseline)."""
+    t0 = time.time()
+    inp = wk.generate(wl, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] generated {wl.name} inputs in {time.time() - t0:.1f}s")
+    prob = dsa.Problem.from_workload(wl, inp, device=dev)
+    L, ld = wl.seq_len, prob.ld_scores()
+    scores = torch.empty(L, ld, dtype=torch.float32, device=dev)
+    idx = torch.empty(L, wl.topk, dtype=torch.int32, device=dev)
+    out = torch.empty(L, wl.heads, wl.d_latent, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(L, wl.heads, dtype=torch.float32, device=dev)
+    nt, na = dsa.workspace_bytes(prob, dsa.WS_TOPK), dsa.workspace_bytes(prob, dsa.WS_ATTN)
+    tws = torch.empty(nt, dtype=torch.uint8, device=dev) if nt else None
+    aws = torch.empty(na, dtype=torch.uint8, device=dev) if na else None
+
+    def run(ev):
+        ev[0].record()
+        dsa.indexer_scores(prob, inp["q_fp8"], inp["q_scale"], inp["w"], inp["k_fp8"], inp["k_scale"],
+                           scores, ld)
+        ev[1].record()
+        dsa.topk(prob, scores, idx, ld=ld, workspace=tws)
+        ev[2].record()
+        dsa.sparse_attn(prob, inp["q"], inp["kv"], idx, out, lse, workspace=aws)
+        ev[3].record()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(warmup + iters)]
+    for i in range(warmup + iters):
+        flush()
+        run(evs[i])
+    torch.cuda.synchronize()
+    t = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs[warmup:]])
+    med = np.median(t, axis=0)
+    total = float(np.median(t.sum(axis=1)))
+    pos = np.arange(L)
+    stages = {"indexer": stage_entry(med[0], 1, "mfma", indexer_flops(wl, pos), peaks),
+              "topk": stage_entry(med[1], 1, "hbm", topk_bytes(wl, pos), peaks),
+              "sparse_attn": stage_entry(med[2], 1, "hbm", attn_bytes(wl, pos), peaks,
+                                         bf16_flops=attn_flops(wl, pos))}
+    log(f"[bench] {wl.name}: {total:.3f} ms per pass (indexer {med[0]:.3f}, top-k {med[1]:.3f}, "
+        f"attention {med[2]:.3f} ms), MALL flushed between passes")
+    res = {"workload": wl.name, "tokens_per_s": round(L / (total * 1e-3), 1), "ms": round(total, 4),
+           "iters": iters, "mall_flushed": True, "stages": stages}
+    del scores, out, lse, tws, aws
+    return res, inp, idx
 
 
 def run_train(bench, steps=2):
@@ -326,11 +466,7 @@ def train_cpu_baseline(bench, wl, rows_n=512, batch=32):
     Rows are copied to the host a batch at a time (untimed); only the oracle
     calls are timed."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    threads = _blas_threads()
     inp, L, C = bench.inp, wl.seq_len, wl.chunk
     r0 = L - C
     rows_all = np.linspace(0, C - 1, rows_n).astype(np.int64)
@@ -422,14 +558,62 @@ def run_decode(args, dev):
     return us, us_paged, inp
 
 
+def run_decode_stages(inp, dev, flush, peaks=None, iters=20, warmup=3):
+    """The decode step stage by stage (indexer, top-k, attention through the
+    stage calls, each bracketed by events) and whole (dsa_forward), each
+    iteration after a MALL flush, as a decode step that follows other work
+    would run.  Medians."""
+    wl = wk.DECODE_B64
+    prob = dsa.Problem.from_workload(wl, inp, device=dev)
+    B, ld = wl.decode_batch, prob.ld_scores()
+    scores = torch.empty(B, ld, dtype=torch.float32, device=dev)
+    out = torch.empty(B, wl.heads, wl.d_latent, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(B, wl.heads, dtype=torch.float32, device=dev)
+    idx = torch.empty(B, wl.topk, dtype=torch.int32, device=dev)
+    nt, na = dsa.workspace_bytes(prob, dsa.WS_TOPK), dsa.workspace_bytes(prob, dsa.WS_ATTN)
+    tws = torch.empty(nt, dtype=torch.uint8, device=dev) if nt else None
+    aws = torch.empty(na, dtype=torch.uint8, device=dev) if na else None
+    fws = torch.empty(dsa.workspace_bytes(prob, dsa.WS_FORWARD), dtype=torch.uint8, device=dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(warmup + iters)]
+    for i in range(warmup + iters):
+        e = ev[i]
+        flush()
+        e[0].record()
+        dsa.indexer_scores(prob, inp["q_fp8"], inp["q_scale"], inp["w"], inp["k_fp8"], inp["k_scale"],
+                           scores, ld)
+        e[1].record()
+        dsa.topk(prob, scores, idx, ld=ld, workspace=tws)
+        e[2].record()
+        dsa.sparse_attn(prob, inp["q"], inp["kv"], idx, out, lse, workspace=aws)
+        e[3].record()
+        flush()
+        e[4].record()
+        dsa.forward(prob, inp["q_fp8"], inp["q_scale"], inp["w"], inp["k_fp8"], inp["k_scale"],
+                    inp["q"], inp["kv"], out, lse, idx, fws)
+        e[5].record()
+    torch.cuda.synchronize()
+    t = np.array([[e[j].elapsed_time(e[j + 1]) for j in (0, 1, 2, 4)] for e in ev[warmup:]])
+    med = np.median(t, axis=0)
+    pos = np.asarray(inp["q_pos0"], dtype=np.int64)
+    stages = {"indexer": stage_entry(med[0], 1, "hbm", indexer_decode_bytes(wl, pos), peaks),
+              "topk": stage_entry(med[1], 1, "hbm", topk_bytes(wl, pos), peaks),
+              "sparse_attn": stage_entry(med[2], 1, "hbm", attn_bytes(wl, pos), peaks,
+                                         bf16_flops=attn_flops(wl, pos))}
+    for v in stages.values():
+        v["us"] = round(v.pop("ms_per_step") * 1e3, 1)
+        v.pop("launches_per_step")
+        v.pop("avg_launch_us")
+    ideal = (indexer_decode_bytes(wl, pos) + topk_bytes(wl, pos) + attn_bytes(wl, pos)) / HBM_PEAK
+    log(f"[bench] decode stages after a MALL flush: indexer {med[0] * 1e3:.1f} us, top-k "
+        f"{med[1] * 1e3:.1f} us, attention {med[2] * 1e3:.1f} us; dsa_forward {med[3] * 1e3:.1f} us")
+    return {"forward_us_mall_flushed": round(med[3] * 1e3, 1), "stages": stages,
+            "ideal_us_at_hbm_peak": round(ideal * 1e6, 1), "iters": iters}
+
+
 def cpu_baseline(bench, wl, rows_n):
     """The float64 oracle on a stratified sample of query rows of the prefill."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    threads = _blas_threads()
     inp = bench.inp
     L = wl.seq_len
     rng = np.random.default_rng(wl.seed)
@@ -457,6 +641,91 @@ def cpu_baseline(bench, wl, rows_n):
             "seconds": round(dt, 2)}
 
 
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return None
+
+
+def _oracle_prefill_rows(inp, wl, rows, block=512):
+    """Time the oracle's forward over packed prefill rows (host copies made per
+    block, untimed); returns seconds."""
+    import oracle
+    kd = oracle.dequantize(inp["k_fp8"].cpu().numpy(), inp["k_scale"].cpu().numpy())
+    kv = inp["kv"].cpu().double().numpy()
+    dt = 0.0
+    for b0 in range(0, len(rows), block):
+        r = rows[b0:b0 + block]
+        at = torch.as_tensor(r)
+        qd = oracle.dequantize(inp["q_fp8"][at].cpu().numpy(), inp["q_scale"][at].cpu().numpy())
+        w = inp["w"][at].cpu().double().numpy()
+        qa = inp["q"][at].cpu().double().numpy()
+        t0 = time.perf_counter()
+        oracle.forward_rows(qd, w, kd, r, qa, kv, wl.topk, wl.softmax_scale, wl.d_latent)
+        dt += time.perf_counter() - t0
+    return dt
+
+
+def cpu_baseline_configs(dev, prefill_4k_inp=None, decode_inp=None):
+    """The oracle over every row of the tiny prefill and the 4K prefill, and
+    every sequence of the decode batch, on the inputs the GPU ran."""
+    import oracle
+    res = {}
+    for wl, inp in ((wk.TINY_PREFILL, None), (wk.PREFILL_4K, prefill_4k_inp)):
+        if inp is None:
+            inp = wk.generate(wl, device=dev)
+        L = wl.seq_len
+        dt = _oracle_prefill_rows(inp, wl, np.arange(L))
+        res[wl.name] = {"value": round(L / dt, 2), "unit": "tokens/s", "seconds": round(dt, 2),
+                        "rows": L, "sample": "every query row"}
+        log(f"[bench] cpu baseline {wl.name}: {dt:.1f}s for all {L} rows")
+    if decode_inp is not None:
+        wl, inp = wk.DECODE_B64, decode_inp
+        dt = 0.0
+        for b in range(wl.decode_batch):
+            k0, k1 = inp["kv_offsets"][b], inp["kv_offsets"][b + 1]
+            kd = oracle.dequantize(inp["k_fp8"][k0:k1].cpu().numpy(), inp["k_scale"][k0:k1].cpu().numpy())
+            kv = inp["kv"][k0:k1].cpu().double().numpy()
+            qd = oracle.dequantize(inp["q_fp8"][b:b + 1].cpu().numpy(), inp["q_scale"][b:b + 1].cpu().numpy())
+            w = inp["w"][b:b + 1].cpu().double().numpy()
+            qa = inp["q"][b:b + 1].cpu().double().numpy()
+            t0 = time.perf_counter()
+            oracle.forward_rows(qd, w, kd, [k1 - k0 - 1], qa, kv, wl.topk, wl.softmax_scale, wl.d_latent)
+            dt += time.perf_counter() - t0
+        res[wl.name] = {"value": round(dt * 1e6, 1), "unit": "us/step", "seconds": round(dt, 2),
+                        "rows": wl.decode_batch, "sample": "every sequence of the batch"}
+        log(f"[bench] cpu baseline {wl.name}: {dt:.1f}s for all {wl.decode_batch} sequences")
+    return res
+
+
+def cpu_baseline_single_thread(bench, wl, rows_n=48):
+    """The oracle on a small sample of the 128K prefill's rows with one BLAS
+    thread, scaled to tokens/s like the headline baseline."""
+    from threadpoolctl import threadpool_limits
+    L = wl.seq_len
+    rows = np.linspace(0, L - 1, rows_n).astype(np.int64)
+    with threadpool_limits(limits=1):
+        dt = _oracle_prefill_rows(bench.inp, wl, rows)
+    frac = float(np.sum(rows + 1)) / float(np.sum(np.arange(1, L + 1))) * L / len(rows)
+    log(f"[bench] single-thread cpu baseline: {dt:.1f}s for {rows_n} rows")
+    return {"value": round(len(rows) * frac / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{rows_n} query rows spread evenly over the 131072-token sequence, one BLAS "
+                      f"thread, scaled like cpu_baseline", "seconds": round(dt, 2)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -464,8 +733,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-train", action="store_true", help="skip the alignment-loss training step")
+    ap.add_argument("--no-small-prefill", action="store_true", help="skip the 4K and 32K prefills")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--only", choices=("prefill", "train", "decode", "small_prefill"), default=None,
+                    help="run only this part (for profiling runs; the headline fields are then "
+                         "null unless the part is the 128K prefill)")
     ap.add_argument("--stages-json", default=None, help="also write per-chunk stage times here")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for scaling HBM byte counters)")
@@ -489,30 +762,59 @@ def main():
         print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "copies": 3}))
         return
     dsa.load_library()
-    bench, wl, value, ms_per_step, stages, per_chunk = run_prefill(args, dev)
-    dominant = max(stages, key=lambda s: stages[s]["ms_per_step"])
-    d = stages[dominant]
-    traffic = measured_traffic(dominant)
-    roofline = {"bound": d["bound"], "achieved": d["achieved"], "peak": d["peak"],
-                "unit": d["unit"], "frac": d["frac"], "traffic": traffic, "kernel": dominant,
-                "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)"}
+    only = args.only
+    do = {"prefill": only in (None, "prefill", "train"),
+          "train": (only is None and not args.no_train) or only == "train",
+          "decode": (only is None and not args.no_decode) or only == "decode",
+          "small_prefill": (only is None and not args.no_small_prefill) or only == "small_prefill"}
+    cpu_on = only is None and not args.no_cpu_baseline
+    peaks = measured_peaks(dev) if only is None else None
+    if peaks:
+        log(f"[bench] measured peaks: {peaks}")
+    flush = MallFlush(dev)
+    wl = wk.CHUNKED_PREFILL_128K
+    bench = value = ms_per_step = stages = roofline = None
+    if do["prefill"]:
+        bench, wl, value, ms_per_step, stages, per_chunk = run_prefill(args, dev, peaks)
+        dominant = max(stages, key=lambda s: stages[s]["ms_per_step"])
+        d = stages[dominant]
+        roofline = {"bound": d["bound"], "achieved": d["achieved"], "peak": d["peak"],
+                    "unit": d["unit"], "frac": d["frac"], "traffic": measured_traffic(dominant),
+                    "kernel": dominant,
+                    "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)"}
+        if "frac_measured" in d:
+            roofline["frac_measured"] = d["frac_measured"]
+        if args.stages_json:
+            with open(args.stages_json, "w") as f:
+                json.dump({"stages": stages, "per_chunk_ms": per_chunk.tolist()}, f, indent=1)
     train = None
-    if not args.no_train:
+    if do["train"]:
         train = run_train(bench)
-        if not args.no_cpu_baseline:
+        if cpu_on:
             train["cpu_baseline"] = train_cpu_baseline(bench, wl)
-    decode_us = decode_paged_us = None
-    if not args.no_decode:
-        decode_us, decode_paged_us, _ = run_decode(args, dev)
-    cpu = None
-    if not args.no_cpu_baseline:
+    decode_us = decode_paged_us = decode_stages = decode_inp = None
+    if do["decode"]:
+        decode_us, decode_paged_us, decode_inp = run_decode(args, dev)
+        decode_stages = run_decode_stages(decode_inp, dev, flush, peaks)
+    prefill_configs = {}
+    p4k_inp = None
+    if do["small_prefill"]:
+        for swl in (wk.PREFILL_4K, wk.PREFILL_32K_BOOSTED):
+            res, inp, _ = run_prefill_single(swl, dev, flush, peaks)
+            prefill_configs[swl.name] = res
+            if swl is wk.PREFILL_4K:
+                p4k_inp = inp
+            del inp
+            torch.cuda.empty_cache()
+    cpu = cpu1 = cpu_cfgs = None
+    if cpu_on and bench is not None:
         cpu = cpu_baseline(bench, wl, args.cpu_rows)
-    if args.stages_json:
-        with open(args.stages_json, "w") as f:
-            json.dump({"stages": stages, "per_chunk_ms": per_chunk.tolist()}, f, indent=1)
+        cpu1 = cpu_baseline_single_thread(bench, wl)
+        cpu_cfgs = cpu_baseline_configs(dev, p4k_inp, decode_inp)
     line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 3),
+        "metric": METRIC, "value": None if value is None else round(value, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": None if ms_per_step is None else round(ms_per_step, 3),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "fp8e4m3+bf16", "data": "synthetic",
         "config": {"workload": wl.name, "seq_len": wl.seq_len, "chunk": wl.chunk,
@@ -523,10 +825,17 @@ def main():
         "decode_paged_us_per_step": None if decode_paged_us is None else round(decode_paged_us, 1),
         "decode_config": {"workload": wk.DECODE_B64.name, "batch": 64,
                           "ctx": [wk.DECODE_B64.ctx_min, wk.DECODE_B64.ctx_max]},
+        "decode_stages": decode_stages,
         "roofline": roofline,
         "stages": stages,
+        "prefill_configs": prefill_configs or None,
+        "measured_peaks": peaks,
         "train_align": train,
         "cpu_baseline": cpu,
+        "cpu_baseline_single_thread": cpu1,
+        "cpu_baseline_configs": cpu_cfgs,
+        "cpu_model": cpu_model(),
+        "cpu_threads": _blas_threads(),
     }
     print(json.dumps(line), flush=True)
 
