@@ -7,8 +7,9 @@ selector and the sparse MLA attention against its full causal prefix
 ``value`` is prefill tokens/s over the K timed steps, with every input
 already resident in HBM.  The same run also times the decode step (64
 sequences, cached contexts uniform in [8K, 128K]) and reports it as
-``decode_us_per_step``, and the same decode step over paged caches (64-row
-blocks, shuffled) as ``decode_paged_us_per_step``.  ``train_align`` times the
+``decode_us_per_step``, the same decode step over paged caches (64-row
+blocks, shuffled) as ``decode_paged_us_per_step``, and with the indexer and
+the selector fused (dsa_forward_fused) as ``decode_fused_us_per_step``.  ``train_align`` times the
 sparse-stage training step: the same 32 chunks, each followed by the indexer
 alignment loss over its selected keys (loss and score gradient per row) and
 the indexer backward (that gradient carried to dq, dw and dk).
@@ -555,7 +556,26 @@ def run_decode(args, dev):
     us_paged = a.elapsed_time(b) * 1e3 / n
     log(f"[bench] decode step over paged caches {us_paged:.1f} us")
     del kc, ksc, kvc
-    return us, us_paged, inp
+
+    # The same step with the indexer and the selector fused (dsa_forward_fused).
+    fws = torch.empty(dsa.workspace_bytes(prob, dsa.WS_FORWARD_FUSED), dtype=torch.uint8, device=dev)
+
+    def step_fused():
+        dsa.forward_fused(prob, inp["q_fp8"], inp["q_scale"], inp["w"], inp["k_fp8"], inp["k_scale"],
+                          inp["q"], inp["kv"], out, lse, idx, fws)
+
+    for _ in range(3):
+        step_fused()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(n):
+        step_fused()
+    b.record()
+    torch.cuda.synchronize()
+    us_fused = a.elapsed_time(b) * 1e3 / n
+    log(f"[bench] decode step with the fused indexer and top-k {us_fused:.1f} us")
+    del fws
+    return us, us_paged, us_fused, inp
 
 
 def run_decode_stages(inp, dev, flush, peaks=None, iters=20, warmup=3):
@@ -792,9 +812,9 @@ def main():
         train = run_train(bench)
         if cpu_on:
             train["cpu_baseline"] = train_cpu_baseline(bench, wl)
-    decode_us = decode_paged_us = decode_stages = decode_inp = None
+    decode_us = decode_paged_us = decode_fused_us = decode_stages = decode_inp = None
     if do["decode"]:
-        decode_us, decode_paged_us, decode_inp = run_decode(args, dev)
+        decode_us, decode_paged_us, decode_fused_us, decode_inp = run_decode(args, dev)
         decode_stages = run_decode_stages(decode_inp, dev, flush, peaks)
     prefill_configs = {}
     p4k_inp = None
@@ -823,6 +843,7 @@ def main():
                    "parallelism": "single GPU"},
         "decode_us_per_step": None if decode_us is None else round(decode_us, 1),
         "decode_paged_us_per_step": None if decode_paged_us is None else round(decode_paged_us, 1),
+        "decode_fused_us_per_step": None if decode_fused_us is None else round(decode_fused_us, 1),
         "decode_config": {"workload": wk.DECODE_B64.name, "batch": 64,
                           "ctx": [wk.DECODE_B64.ctx_min, wk.DECODE_B64.ctx_max]},
         "decode_stages": decode_stages,

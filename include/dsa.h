@@ -77,7 +77,8 @@ typedef struct dsa_problem {
 } dsa_problem;
 
 /* Workspace selectors for dsa_workspace_bytes(). */
-enum { DSA_WS_TOPK = 0, DSA_WS_ATTN = 1, DSA_WS_FORWARD = 2, DSA_WS_INDEXER_BWD = 3 };
+enum { DSA_WS_TOPK = 0, DSA_WS_ATTN = 1, DSA_WS_FORWARD = 2, DSA_WS_INDEXER_BWD = 3,
+       DSA_WS_FORWARD_FUSED = 4 };
 
 /*
  * Stage 1, lightning indexer (r.nikiv.dev summary, "How DSA Works"; the
@@ -156,9 +157,10 @@ dsa_status dsa_sparse_attn(const dsa_problem *p, const uint16_t *q, const uint16
 
 /*
  * The three stages in order (indexer -> top-k -> attention) on one stream.
- * Arguments as in the stage calls.  The scores matrix lives in the workspace;
- * topk_idx_out (nullable) receives the selected positions when given,
- * otherwise they also live in the workspace.
+ * Arguments as in the stage calls; the results equal the three calls'.  The
+ * scores matrix lives at the start of the workspace (ld_scores = max_kv_len
+ * rounded up to a multiple of 64); topk_idx_out (nullable) receives the
+ * selected positions when given, otherwise they also live in the workspace.
  * workspace: at least dsa_workspace_bytes(p, DSA_WS_FORWARD) bytes.
  */
 dsa_status dsa_forward(const dsa_problem *p, const uint8_t *q_fp8, const float *q_scale,
@@ -208,6 +210,32 @@ dsa_status dsa_sparse_attn_paged(const dsa_problem *p, const dsa_paged_kv *pg, c
 dsa_status dsa_forward_paged(const dsa_problem *p, const dsa_paged_kv *pg, const uint8_t *q_fp8,
                              const float *q_scale, const float *w, const uint8_t *k_cache,
                              const float *ks_cache, const uint16_t *q, const uint16_t *kv_cache,
+                             uint16_t *out, float *lse, int32_t *topk_idx_out, void *workspace,
+                             size_t workspace_bytes, void *stream);
+
+/*
+ * dsa_forward with the indexer and the selector fused, for decode-shaped
+ * problems: at most two query rows per sequence, rows of at most 262144 keys
+ * (others: DSA_ERR_UNSUPPORTED).  The indexer's scores serve only the top-k
+ * selection (r.nikiv.dev summary, "How DSA Works"), so instead of a scores
+ * matrix each 1024-key chunk of a row leaves its keys grouped by their
+ * leading 12 bits (an eighth-of-an-octave bin of the score) with a table of
+ * its bins; the selection adds up the tables, finds the bin holding the k-th
+ * largest score exactly, reads only the keys at or above that bin, and
+ * resolves that bin and its ties (lowest position first) among them.  The
+ * indices, outputs and lse are bit-identical to dsa_forward's.  No scores
+ * are kept.  pg: NULL for packed caches, else the paged caches as for
+ * dsa_forward_paged (k_fp8, k_scale and kv are then the caches).
+ * workspace: at least dsa_workspace_bytes(p, DSA_WS_FORWARD_FUSED) bytes
+ * (about 8 KB per (query row, 1024 keys of max_kv_len), plus the indices and
+ * the attention's share).
+ * On MI355X this form is slower than dsa_forward for the 64-sequence decode
+ * batch: binning inside the bandwidth-bound decode indexer lengthens it by
+ * more than the cheaper selection saves.
+ */
+dsa_status dsa_forward_fused(const dsa_problem *p, const dsa_paged_kv *pg, const uint8_t *q_fp8,
+                             const float *q_scale, const float *w, const uint8_t *k_fp8,
+                             const float *k_scale, const uint16_t *q, const uint16_t *kv,
                              uint16_t *out, float *lse, int32_t *topk_idx_out, void *workspace,
                              size_t workspace_bytes, void *stream);
 
@@ -323,8 +351,9 @@ dsa_status dsa_forward_noalloc(const dsa_problem *p, const uint8_t *q_fp8, const
                                int32_t *topk_idx_out, void *stream);
 
 /* Bytes of device workspace the given entry point needs for problem p
- * (which = DSA_WS_TOPK, DSA_WS_ATTN, DSA_WS_FORWARD, or DSA_WS_INDEXER_BWD
- * for the two-pass form of dsa_indexer_backward); 0 if none.  Returns
+ * (which = DSA_WS_TOPK, DSA_WS_ATTN, DSA_WS_FORWARD, DSA_WS_FORWARD_FUSED, or
+ * DSA_WS_INDEXER_BWD for the two-pass form of dsa_indexer_backward); 0 if
+ * none.  Returns
  * (size_t)-1 for an invalid problem (see dsa_last_error).  The paged entry
  * points need the same amounts. */
 size_t dsa_workspace_bytes(const dsa_problem *p, int which);

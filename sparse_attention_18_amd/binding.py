@@ -23,12 +23,12 @@ DSA_ERR_INVALID_ARGUMENT = 1
 DSA_ERR_UNSUPPORTED = 2
 DSA_ERR_WORKSPACE = 3
 DSA_ERR_HIP = 4
-WS_TOPK, WS_ATTN, WS_FORWARD, WS_INDEXER_BWD = 0, 1, 2, 3
+WS_TOPK, WS_ATTN, WS_FORWARD, WS_INDEXER_BWD, WS_FORWARD_FUSED = 0, 1, 2, 3, 4
 
 EXPORTED = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward",
             "dsa_indexer_scores_paged", "dsa_sparse_attn_paged", "dsa_forward_paged",
             "dsa_indexer_align_loss", "dsa_indexer_backward", "dsa_workspace_bytes", "dsa_last_error", "dsa_version",
-            "dsa_forward_noalloc")
+            "dsa_forward_noalloc", "dsa_forward_fused")
 NOALLOC_SCRATCH_BYTES = 256 << 20      # DSA_NOALLOC_SCRATCH_BYTES in include/dsa.h
 
 
@@ -107,9 +107,11 @@ def load_library():
         lib.dsa_indexer_align_loss.argtypes = [P, vp, vp, vp, vp, i64, vp, vp, vp, i64, vp]
         lib.dsa_indexer_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]
         lib.dsa_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+        lib.dsa_forward_fused.argtypes = [P, G, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward",
                      "dsa_indexer_scores_paged", "dsa_sparse_attn_paged", "dsa_forward_paged",
-                     "dsa_indexer_align_loss", "dsa_indexer_backward", "dsa_forward_noalloc"):
+                     "dsa_indexer_align_loss", "dsa_indexer_backward", "dsa_forward_noalloc",
+                     "dsa_forward_fused"):
             getattr(lib, name).restype = ctypes.c_int
         lib.dsa_workspace_bytes.argtypes = [P, ctypes.c_int]
         lib.dsa_workspace_bytes.restype = sz
@@ -301,6 +303,35 @@ def forward_noalloc(prob: Problem, q_fp8, q_scale, w, k_fp8, k_scale, q, kv, out
         _ptr(out, torch.bfloat16, "out", (c.total_q, c.heads, c.d_latent)),
         _ptr(lse, torch.float32, "lse", (c.total_q, c.heads)),
         _ptr(idx_out, torch.int32, "idx_out", (c.total_q, c.topk)), _stream(stream)))
+
+
+def forward_fused(prob: Problem, q_fp8, q_scale, w, k_fp8, k_scale, q, kv, out, lse=None,
+                  idx_out=None, workspace=None, pg: "PagedKV" = None, stream=None):
+    """dsa_forward_fused: the forward with the indexer and the selector fused
+    (decode-shaped problems); ``workspace`` holds at least
+    ``workspace_bytes(prob, WS_FORWARD_FUSED)`` bytes.  With ``pg`` the key and
+    KV arguments are the paged caches."""
+    c = prob.c
+    D = c.d_latent + c.d_rope
+    if workspace is None:
+        raise ValueError("forward_fused needs a workspace tensor")
+    if pg is None:
+        ksh, ssh, vsh = (c.total_kv, c.idx_dim), (c.total_kv,), (c.total_kv, D)
+    else:
+        ksh, ssh, vsh = _cache_shapes(c, pg)
+    _check(load_library().dsa_forward_fused(
+        ctypes.byref(c), ctypes.byref(pg.c) if pg is not None else None,
+        _ptr(q_fp8, torch.uint8, "q_fp8", (c.total_q, c.idx_heads, c.idx_dim)),
+        _ptr(q_scale, torch.float32, "q_scale", (c.total_q,)),
+        _ptr(w, torch.float32, "w", (c.total_q, c.idx_heads)),
+        _ptr(k_fp8, torch.uint8, "k_fp8", ksh),
+        _ptr(k_scale, torch.float32, "k_scale", ssh),
+        _ptr(q, torch.bfloat16, "q", (c.total_q, c.heads, D)),
+        _ptr(kv, torch.bfloat16, "kv", vsh),
+        _ptr(out, torch.bfloat16, "out", (c.total_q, c.heads, c.d_latent)),
+        _ptr(lse, torch.float32, "lse", (c.total_q, c.heads)),
+        _ptr(idx_out, torch.int32, "idx_out", (c.total_q, c.topk)),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
 
 
 def indexer_align_loss(prob: Problem, q, kv, lse, scores, loss, grad, idx=None, ld=None,

@@ -201,6 +201,7 @@ dsa::TopkArgs topk_args(const dsa_problem *p, const float *scores, int64_t ld, i
   a.workspace_bytes = wsb;
   a.seg_len = 0;
   a.nseg = 0;
+  a.fuse = dsa::FuseArgs{};
   return a;
 }
 
@@ -219,6 +220,7 @@ dsa::IndexerArgs indexer_args(const dsa_problem *p, const uint8_t *q_fp8, const 
   a.ld = ld;
   a.idx_heads = p->idx_heads;
   a.idx_dim = p->idx_dim;
+  a.fuse = dsa::FuseArgs{};
   return a;
 }
 
@@ -260,18 +262,37 @@ size_t ws_indexer_bwd(const dsa_problem *p) {
 }
 
 // Layout of dsa_forward's workspace: scores | indices | top-k scratch | attention scratch.
+// dsa_forward_fused selects from what the decode indexer leaves per 1024-key
+// chunk instead of from scores: no scores region, and the top-k scratch holds
+// the chunks' data.
 struct ForwardWs {
   size_t scores, idx, topk, attn, total;
+  bool fused;
 };
-ForwardWs forward_ws(const dsa_problem *p) {
+ForwardWs forward_ws(const dsa_problem *p, bool fuse = false) {
   ForwardWs w;
   const int64_t ld = forward_ld(p);
-  w.scores = round_up((size_t)p->total_q * (size_t)ld * sizeof(float), 256);
+  const dsa::SeqLayout L = layout_of(p);
+  w.fused = fuse && dsa::fuse_eligible(L);
+  w.scores = w.fused ? 0 : round_up((size_t)p->total_q * (size_t)ld * sizeof(float), 256);
   w.idx = round_up((size_t)p->total_q * (size_t)p->topk * sizeof(int32_t), 256);
-  w.topk = round_up(ws_topk(p, ld), 256);
+  w.topk = round_up(w.fused ? dsa::fuse_workspace_bytes(L) : ws_topk(p, ld), 256);
   w.attn = round_up(ws_attn(p), 256);
   w.total = w.scores + w.idx + w.topk + w.attn;
   return w;
+}
+
+// The fused top-k's buffers inside the top-k scratch (fuse_workspace_bytes).
+dsa::FuseArgs fuse_layout(const dsa_problem *p, void *base) {
+  dsa::FuseArgs f;
+  f.nchunk = (int32_t)((p->max_kv_len + dsa::kFuseChunk - 1) / dsa::kFuseChunk);
+  const size_t slots = (size_t)p->total_q * (size_t)f.nchunk;
+  uint8_t *b = static_cast<uint8_t *>(base);
+  f.tab = reinterpret_cast<uint32_t *>(b);
+  f.nz = reinterpret_cast<uint32_t *>(b + round_up(slots * dsa::kFuseTabCap * 4, 256));
+  f.list = reinterpret_cast<uint32_t *>(b + round_up(slots * dsa::kFuseTabCap * 4, 256) +
+                                        round_up(slots * 4, 256));
+  return f;
 }
 
 }  // namespace
@@ -288,6 +309,13 @@ size_t dsa_workspace_bytes(const dsa_problem *p, int which) {
     case DSA_WS_TOPK: return ws_topk(p, forward_ld(p));
     case DSA_WS_ATTN: return ws_attn(p);
     case DSA_WS_FORWARD: return forward_ws(p).total;
+    case DSA_WS_FORWARD_FUSED:
+      if (!dsa::fuse_eligible(layout_of(p))) {
+        fail(DSA_ERR_UNSUPPORTED, "dsa_forward_fused serves at most two query rows per sequence "
+             "and rows of at most %lld keys", (long long)dsa::kFuseMaxLen);
+        return (size_t)-1;
+      }
+      return forward_ws(p, true).total;
     case DSA_WS_INDEXER_BWD: return ws_indexer_bwd(p);
     default: fail(DSA_ERR_INVALID_ARGUMENT, "unknown workspace selector %d", which); return (size_t)-1;
   }
@@ -374,15 +402,18 @@ dsa_status forward_impl(const dsa_problem *p, const dsa_paged_kv *pg, const uint
                         const float *q_scale, const float *w, const uint8_t *k_fp8,
                         const float *k_scale, const uint16_t *q, const uint16_t *kv, uint16_t *out,
                         float *lse, int32_t *topk_idx_out, void *workspace, size_t workspace_bytes,
-                        void *stream) {
+                        void *stream, bool fuse = false) {
   DSA_TRY(check_problem(p));
   if (pg != nullptr) DSA_TRY(check_paged(p, pg));
   DSA_TRY(check_indexer_dims(p));
   DSA_TRY(check_attn_dims(p, pg != nullptr));
+  DSA_CHECK(!fuse || dsa::fuse_eligible(layout_of(p)), DSA_ERR_UNSUPPORTED,
+            "dsa_forward_fused serves at most two query rows per sequence and rows of at most "
+            "%lld keys", (long long)dsa::kFuseMaxLen);
   DSA_TRY(check_indexer_ptrs(p, q_fp8, q_scale, w, k_fp8, k_scale));
   DSA_TRY(check_attn_ptrs(p, q, kv, out, lse));
   if (topk_idx_out != nullptr) DSA_TRY(check_ptr(topk_idx_out, p->total_q > 0, "topk_idx_out"));
-  const ForwardWs ws = forward_ws(p);
+  const ForwardWs ws = forward_ws(p, fuse);
   DSA_CHECK(workspace_bytes >= ws.total && workspace != nullptr, DSA_ERR_WORKSPACE,
             "forward workspace needs %zu bytes (got %zu)", ws.total, workspace_bytes);
   DSA_CHECK(aligned16(workspace), DSA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
@@ -394,10 +425,11 @@ dsa_status forward_impl(const dsa_problem *p, const dsa_paged_kv *pg, const uint
   void *topk_ws = base + ws.scores + ws.idx;
   void *attn_ws = base + ws.scores + ws.idx + ws.topk;
   const int64_t ld = forward_ld(p);
-  DSA_TRY(hip_status(dsa::launch_indexer(indexer_args(p, q_fp8, q_scale, w, k_fp8, k_scale,
-                                                      scores, ld, pg), st),
-                     "indexer launch"));
-  DSA_TRY(hip_status(dsa::launch_topk(topk_args(p, scores, ld, idx, topk_ws, ws.topk), st),
+  dsa::IndexerArgs ia = indexer_args(p, q_fp8, q_scale, w, k_fp8, k_scale, scores, ld, pg);
+  dsa::TopkArgs ta = topk_args(p, scores, ld, idx, topk_ws, ws.topk);
+  if (ws.fused) ia.fuse = ta.fuse = fuse_layout(p, topk_ws);
+  DSA_TRY(hip_status(dsa::launch_indexer(ia, st), "indexer launch"));
+  DSA_TRY(hip_status(ws.fused ? dsa::launch_topk_fused(ta, st) : dsa::launch_topk(ta, st),
                      "top-k launch"));
   return hip_status(dsa::launch_sparse_attn(attn_args(p, q, kv, idx, out, lse, attn_ws, ws.attn, pg),
                                             st),
@@ -438,6 +470,15 @@ dsa_status dsa_forward_paged(const dsa_problem *p, const dsa_paged_kv *pg, const
   if (pg == nullptr) return fail(DSA_ERR_INVALID_ARGUMENT, "paged-cache description is NULL");
   return forward_impl(p, pg, q_fp8, q_scale, w, k_cache, ks_cache, q, kv_cache, out, lse,
                       topk_idx_out, workspace, workspace_bytes, stream);
+}
+
+dsa_status dsa_forward_fused(const dsa_problem *p, const dsa_paged_kv *pg, const uint8_t *q_fp8,
+                             const float *q_scale, const float *w, const uint8_t *k_fp8,
+                             const float *k_scale, const uint16_t *q, const uint16_t *kv,
+                             uint16_t *out, float *lse, int32_t *topk_idx_out, void *workspace,
+                             size_t workspace_bytes, void *stream) {
+  return forward_impl(p, pg, q_fp8, q_scale, w, k_fp8, k_scale, q, kv, out, lse, topk_idx_out,
+                      workspace, workspace_bytes, stream, true);
 }
 
 }  // extern "C"

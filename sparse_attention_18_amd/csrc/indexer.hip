@@ -311,12 +311,98 @@ void indexer_prefill_kernel(IndexerArgs p, int key_split) {
   }
 }
 
+// ---- Selection data for the fused top-k (decode).  Each 1024-key chunk of
+// a row bins its scores by the top 12 bits of their order-preserving keys
+// (sign, exponent and three mantissa bits: 4096 bins, an eighth of an octave
+// wide) and leaves, for the row's select kernel (topk.hip):
+//  * a table of its nonzero bins in descending order, one word each:
+//      bin << 20 | (first list slot of the bin) << 10 | (count - 1)
+//    (a chunk has at most 1024 keys, so at most 1024 entries), and its length;
+//  * its keys grouped by bin in that order, one word each:
+//      (low 20 bits of the order key) << 10 | position within the chunk.
+// The bins of the chunk's largest keys come first, so the select reads only
+// the prefix of each list down to the bin that holds the row's k-th key; the
+// lists replace the scores, which this path does not store.
+__device__ __forceinline__ uint32_t fuse_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;                 // -0.0 ranks as +0.0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// LDS operations of one wave complete in issue order; waiting for them all
+// makes this wave's LDS writes visible to its next reads of other addresses.
+__device__ __forceinline__ void lds_drain() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Run by one wave (the chunk's last to finish its keys) over the nloc
+// (>= 1) scores in `sc`, using `hist` (kFuseBins words of LDS) as scratch;
+// the other waves of the workgroup may already have exited.
+__device__ __forceinline__ void bin_chunk(float *sc, uint32_t *hist, int nloc, int lane, uint32_t *tab,
+                                          uint32_t *nz, uint32_t *list) {
+  constexpr int kKeys = kFuseChunk / 64, kBins = kFuseBins / 64;   // per lane: 16 keys, 64 bins
+#pragma unroll
+  for (int u = 0; u < kBins / 4; ++u)
+    *reinterpret_cast<v4i *>(&hist[4 * lane + 256 * u]) = v4i{0, 0, 0, 0};
+  uint32_t key[kKeys];
+#pragma unroll
+  for (int u = 0; u < kKeys / 4; ++u) {
+    const v4f sv = *reinterpret_cast<const v4f *>(sc + 4 * lane + 256 * u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) key[4 * u + j] = fuse_order_key(sv[j]);
+  }
+  lds_drain();
+#pragma unroll
+  for (int u = 0; u < kKeys; ++u)
+    if (4 * lane + 256 * (u >> 2) + (u & 3) < nloc) atomicAdd(&hist[key[u] >> 20], 1u);
+  lds_drain();
+  // Lane l owns bins 4095 - 64l .. 4032 - 64l (descending); a wave scan of
+  // (nonzero bins << 16 | keys) gives its first table entry and list slot.
+  uint32_t cnt[kBins], tot = 0, nzb = 0;
+#pragma unroll
+  for (int u = 0; u < kBins / 4; ++u) {
+    const v4i c4 = *reinterpret_cast<const v4i *>(&hist[kFuseBins - 4 - kBins * lane - 4 * u]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      cnt[4 * u + j] = (uint32_t)c4[3 - j];
+      tot += cnt[4 * u + j];
+      nzb += cnt[4 * u + j] != 0u;
+    }
+  }
+  const uint32_t packed = (nzb << 16) | tot;
+  const uint32_t inc = wave_scan<0>(packed);
+  const uint32_t all = (uint32_t)__builtin_amdgcn_readlane((int)inc, 63);
+  uint32_t slot = (inc - packed) & 0xFFFFu, entry = (inc - packed) >> 16;
+#pragma unroll
+  for (int i = 0; i < kBins; ++i) {
+    if (cnt[i] != 0u) {
+      const uint32_t bin = (uint32_t)(kFuseBins - 1 - kBins * lane - i);
+      tab[entry++] = bin << 20 | slot << 10 | (cnt[i] - 1u);
+      hist[bin] = slot;                          // the bin's next free slot
+      slot += cnt[i];
+    }
+  }
+  if (lane == 0) *nz = all >> 16;
+  lds_drain();
+  // Scatter into LDS (over the scores, all read above), then one coalesced copy.
+  uint32_t *lst = reinterpret_cast<uint32_t *>(sc);
+#pragma unroll
+  for (int u = 0; u < kKeys; ++u) {
+    const int li = 4 * lane + 256 * (u >> 2) + (u & 3);
+    if (li < nloc) lst[atomicAdd(&hist[key[u] >> 20], 1u)] = (key[u] & 0xFFFFFu) << 10 | (uint32_t)li;
+  }
+  lds_drain();
+#pragma unroll
+  for (int u = 0; u < kKeys / 4; ++u)
+    if (4 * lane + 256 * u < nloc)
+      *reinterpret_cast<v4i *>(list + 4 * lane + 256 * u) = *reinterpret_cast<const v4i *>(lst + 4 * lane + 256 * u);
+}
+
 // Decode (few query rows per sequence): grid (key chunk, query row).  Keys
 // are used by one query only, so each wave streams its own 256-key slice
 // straight from HBM into MFMA B operands; nothing goes through LDS.
 constexpr int kDecodeChunk = 1024;  // keys per workgroup (4 waves x 256)
+static_assert(kDecodeChunk == kFuseChunk, "a fused chunk is one decode workgroup's keys");
 
-template <int HB, bool kPaged>
+template <int HB, bool kPaged, bool kFuse>
 __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs p) {
   const int64_t row = __builtin_amdgcn_workgroup_id_y();
   SeqInfo s;
@@ -325,8 +411,17 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs p) {
   const int64_t pos = row_pos(s, row);
   const int tid = (int)__builtin_amdgcn_workitem_id_x(), lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
-  const int64_t wave_begin = (int64_t)__builtin_amdgcn_workgroup_id_x() * kDecodeChunk + wave * (kDecodeChunk / kWaves);
-  if (wave_begin > pos) return;
+  const int64_t chunk_begin = (int64_t)__builtin_amdgcn_workgroup_id_x() * kDecodeChunk;
+  if (chunk_begin > pos) return;
+  const int64_t wave_begin = chunk_begin + wave * (kDecodeChunk / kWaves);
+  // A wave past the row's last key has no work (with kFuse it still joins the
+  // workgroup's barriers below).
+  if (!kFuse && wave_begin > pos) return;
+  __shared__ uint32_t s_done;                    // waves that have finished their keys
+  if (kFuse) {
+    if (tid == 0) s_done = 0u;
+    __syncthreads();
+  }
   const int64_t wave_end = wave_begin + kDecodeChunk / kWaves < pos + 1
                                ? wave_begin + kDecodeChunk / kWaves : pos + 1;
 
@@ -337,14 +432,14 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs p) {
   // Keys and key scales are read through buffer descriptors spanning this
   // wave's slice: loads past it return zeros, so every load is issued
   // unconditionally.  The whole offset goes in the vector offset (the scalar
-  // offset is not part of the range check).  With no branch around them the compiler counts them,
-  // and the wait before a step's MFMAs covers only that step's loads; the
-  // next step's stay in flight.  Dims at or past d_I get an offset past the
-  // range (zeros too).  The scores go to LDS and are written out after the
-  // last load: a store between the loads would hold up the waits on them,
-  // which share one in-order counter.
-  __shared__ float s_sc[kWaves][kDecodeChunk / kWaves];
-  const int nk = __builtin_amdgcn_readfirstlane((int)(wave_end - wave_begin));   // 1..256 keys
+  // offset is not part of the range check).  With no branch around them the
+  // compiler counts them, and the wait before a step's MFMAs covers only that
+  // step's loads; the next step's stay in flight.  Dims at or past d_I get an
+  // offset past the range (zeros too).  The scores go to LDS and are written
+  // out after the last load: a store between the loads would hold up the
+  // waits on them, which share one in-order counter.
+  __shared__ __attribute__((aligned(16))) float s_sc[kWaves][kDecodeChunk / kWaves];
+  const int nk = wave_begin > pos ? 0 : __builtin_amdgcn_readfirstlane((int)(wave_end - wave_begin));   // 0..256 keys
   auto rsrc = [&](const void *base, int bytes) {
     const uint64_t a = (uint64_t)(uintptr_t)base;
     const uint64_t u = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a) |
@@ -389,12 +484,12 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs p) {
   };
   // Two register sets take turns (no copy of a set whose loads are still in
   // flight, which would wait for them); loads past the slice read zeros.
-  const int nsteps = (nk + 63) / 64;
+  const int nsteps = (nk + 63) / 64;   // 0 for an idle wave
   v8i ka[4], kb2[4];
   float ksa, ksb;
   // (The scheduling barriers keep each set's loads ahead of the other set's
   // MFMAs.)
-  load_step(0, ka, ksa);
+  if (nsteps > 0) load_step(0, ka, ksa);
   for (int st = 0; st < nsteps; st += 2) {
     load_step(st + 1, kb2, ksb);
     __builtin_amdgcn_sched_barrier(0);
@@ -405,10 +500,24 @@ __global__ __launch_bounds__(256) void indexer_decode_kernel(IndexerArgs p) {
       score_step(st + 1, kb2, ksb);
     }
   }
-  float *srow = p.scores + row * p.ld;
-  for (int64_t t0 = wave_begin; t0 < wave_end; t0 += 64) {
-    const int64_t my_key = t0 + lane;
-    if (my_key < wave_end) srow[my_key] = s_sc[wave][t0 - wave_begin + lane];
+  if constexpr (kFuse) {
+    // The last wave to finish bins the whole chunk; the others leave.
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[kFuseBins];
+    lds_drain();
+    uint32_t done = 0u;
+    if (lane == 0) done = atomicAdd(&s_done, 1u);
+    if (__builtin_amdgcn_readfirstlane(done) != kWaves - 1) return;
+    lds_drain();
+    const int nloc = (int)(pos + 1 - chunk_begin < kDecodeChunk ? pos + 1 - chunk_begin : kDecodeChunk);
+    const int64_t slot = row * p.fuse.nchunk + (int64_t)__builtin_amdgcn_workgroup_id_x();
+    bin_chunk(&s_sc[0][0], s_hist, nloc, lane, p.fuse.tab + slot * kFuseTabCap, p.fuse.nz + slot,
+              p.fuse.list + slot * kDecodeChunk);
+  } else {
+    float *srow = p.scores + row * p.ld;
+    for (int64_t t0 = wave_begin; t0 < wave_end; t0 += 64) {
+      const int64_t my_key = t0 + lane;
+      if (my_key < wave_end) srow[my_key] = s_sc[wave][t0 - wave_begin + lane];
+    }
   }
 }
 
@@ -445,17 +554,22 @@ hipError_t launch_prefill(const IndexerArgs &a, hipStream_t stream) {
 template <int HB>
 hipError_t launch_decode(const IndexerArgs &a, hipStream_t stream) {
   dim3 grid((unsigned)((a.seq.max_kv_len + kDecodeChunk - 1) / kDecodeChunk), (unsigned)a.seq.total_q);
-  if (a.pg.table != nullptr)
-    hipLaunchKernelGGL((indexer_decode_kernel<HB, true>), grid, dim3(256), 0, stream, a);
+  const bool paged = a.pg.table != nullptr, fuse = a.fuse.tab != nullptr;
+  if (paged && fuse)
+    hipLaunchKernelGGL((indexer_decode_kernel<HB, true, true>), grid, dim3(256), 0, stream, a);
+  else if (paged)
+    hipLaunchKernelGGL((indexer_decode_kernel<HB, true, false>), grid, dim3(256), 0, stream, a);
+  else if (fuse)
+    hipLaunchKernelGGL((indexer_decode_kernel<HB, false, true>), grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((indexer_decode_kernel<HB, false>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((indexer_decode_kernel<HB, false, false>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int HB>
 hipError_t dispatch(const IndexerArgs &a, hipStream_t stream) {
   // A handful of query rows per sequence: stream keys per row.
-  if (a.seq.max_q_len <= 2) return launch_decode<HB>(a, stream);
+  if (decode_indexer(a.seq)) return launch_decode<HB>(a, stream);
   return launch_prefill<HB, (HB >= 8 ? 1 : (HB >= 2 ? 2 : 4))>(a, stream);
 }
 

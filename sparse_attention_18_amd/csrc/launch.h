@@ -26,6 +26,22 @@ struct PagedKV {
   int32_t num_blocks;     // num_blocks << block_shift < 2^31
 };
 
+// Fused decode top-k: per (row, 1024-key chunk) slot the decode indexer
+// leaves a table of the chunk's nonzero score bins, its length, and the
+// chunk's keys grouped by bin (instead of the scores); the select kernel
+// reads them.  Rows of at most kFuseMaxLen keys (the select's position
+// bitmaps live in LDS).
+constexpr int kFuseChunk = 1024;       // keys per chunk (one decode indexer workgroup)
+constexpr int kFuseBins = 4096;        // top 12 bits of the order-preserving key
+constexpr int kFuseTabCap = kFuseChunk;   // a chunk has at most this many nonzero bins
+constexpr int64_t kFuseMaxLen = 1 << 18;
+struct FuseArgs {
+  uint32_t *tab;    // [rows * nchunk][kFuseTabCap]; nullptr: no fused selection
+  uint32_t *nz;     // [rows * nchunk]: table entries (nonzero bins) of the chunk
+  uint32_t *list;   // [rows * nchunk][kFuseChunk]
+  int32_t nchunk;   // slots per row: ceil(max_kv_len / kFuseChunk)
+};
+
 struct IndexerArgs {
   SeqLayout seq;
   PagedKV pg;
@@ -37,6 +53,7 @@ struct IndexerArgs {
   float *scores;
   int64_t ld;
   int32_t idx_heads, idx_dim;
+  FuseArgs fuse;    // decode kernel only: also leave the fused top-k's data
 };
 
 struct TopkArgs {
@@ -48,6 +65,7 @@ struct TopkArgs {
   void *workspace;
   size_t workspace_bytes;
   int32_t seg_len, nseg;   // few-rows path: scores per segment, segments per row (set by the launcher)
+  FuseArgs fuse;           // launch_topk_fused: what the decode indexer left
 };
 
 struct AttnArgs {
@@ -116,9 +134,19 @@ hipError_t launch_indexer_backward(const IndexerBwdArgs &a, hipStream_t stream);
 hipError_t launch_align_loss(const AlignArgs &a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs &a, hipStream_t stream);
 hipError_t launch_sparse_attn(const AttnArgs &a, hipStream_t stream);
+// Top-k from the fused data of a decode indexer launch (a.fuse set, a.scores
+// the same launch's scores for the exact fallback).
+hipError_t launch_topk_fused(const TopkArgs &a, hipStream_t stream);
+// Whether the fused decode selection serves a problem, and its workspace.
+bool fuse_eligible(const SeqLayout &seq);
+size_t fuse_workspace_bytes(const SeqLayout &seq);
 size_t sparse_attn_workspace_bytes(const AttnArgs &a);
 size_t topk_workspace_bytes(const TopkArgs &a);
 size_t indexer_bwd_workspace_bytes(const IndexerBwdArgs &a);
+
+// The indexer scores rows with its decode kernel (keys streamed per row, no
+// key tiles shared by queries) when every sequence has at most two query rows.
+inline bool decode_indexer(const SeqLayout &seq) { return seq.max_q_len <= 2; }
 
 // Sequence metadata for one sequence, clamped to the host-validated bounds so
 // that inconsistent device offsets can never produce an out-of-bounds access.

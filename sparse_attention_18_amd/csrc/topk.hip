@@ -557,6 +557,279 @@ void topk_merge_kernel(TopkArgs p, const uint32_t *counts, const uint2 *cands) {
   __syncthreads();
   select_and_emit(total, k, out, sh);
 }
+
+// ---- Fused decode selection.  The decode indexer (indexer.hip, bin_chunk)
+// leaves, per 1024-key chunk of a row, the chunk's nonzero bins of the top 12
+// order-key bits (descending, with each bin's count and first list slot) and
+// its keys grouped by bin.  One workgroup per row then:
+//  1. sums the chunks' bin counts into a 4096-bin row histogram and finds
+//     the bin B1 holding the k-th largest key and the count A above it --
+//     exactly, without a sample and without reading the scores;
+//  2. reads from each chunk's list only the prefix down to B1: the A keys
+//     above B1 (all selected; only their positions are kept) and the E keys
+//     in B1;
+//  3. selects the (k - A)-th largest among the E keys of B1 (radix passes
+//     over their low 20 bits) as the threshold T;
+//  4. marks the selected positions in an LDS bitmap over the row (ties at T
+//     go through a second bitmap, of which the lowest positions are kept)
+//     and writes the set bits in ascending order.
+// The threads are dealt to the row's chunks (tpc per chunk), so every load's
+// address is known without a search.  When more than kCap keys fall in B1
+// they are read from the lists in global memory instead of LDS (exact, slower).
+constexpr int kFuseMaxChunks = (int)(kFuseMaxLen / kFuseChunk);
+constexpr int kFuseWords = (int)(kFuseMaxLen / 32);
+constexpr int kFuseBatch = 8;        // loads in flight per thread
+static_assert(kFuseMaxChunks <= kThreads / 2, "at least two threads per chunk");
+static_assert(kFuseWords % kThreads == 0 && kFuseBins % kThreads == 0, "bitmap and histogram split");
+
+struct FusedShared {
+  union {
+    uint32_t hist[kFuseBins];                     // step 1: row histogram
+    struct {
+      uint32_t sel[kFuseWords];                   // step 4: selected positions
+      uint32_t eq[kFuseWords];                    //         positions whose key is T
+    } bm;
+  };
+  uint32_t above[4096];                           // positions of the A keys above B1 (A < k)
+  uint32_t na[kFuseMaxChunks], ne[kFuseMaxChunks];    // per chunk: keys above B1, keys in B1
+  uint32_t offa[kFuseMaxChunks], offe[kFuseMaxChunks];
+};
+
+// The lowest `r` set bits of x.
+__device__ __forceinline__ uint32_t lowest_set_bits(uint32_t x, uint32_t r) {
+  uint32_t kept = 0u;
+  for (uint32_t i = 0; i < r && x != 0u; ++i) {
+    const uint32_t lsb = x & (0u - x);
+    kept |= lsb;
+    x ^= lsb;
+  }
+  return kept;
+}
+
+__global__ __launch_bounds__(kThreads)
+void topk_fused_kernel(TopkArgs p) {
+  __shared__ TopkShared sh;
+  __shared__ FusedShared fs;
+  const int64_t row = __builtin_amdgcn_workgroup_id_x();
+  SeqInfo s;
+  row_seq(p.seq, row, s);
+  int32_t *out = p.idx + row * p.k;
+  if (row < s.q0 || row >= s.q1 || s.kvlen <= 0) {
+    emit_all(out, 0, p.k);
+    return;
+  }
+  const int64_t n = row_pos(s, row) + 1;       // <= kFuseMaxLen (checked on the host)
+  const int k = p.k;
+  if (n <= k) {
+    emit_all(out, n, k);
+    return;
+  }
+  const int tid = (int)__builtin_amdgcn_workitem_id_x();
+  const int W = (int)((n + kFuseChunk - 1) / kFuseChunk);   // 3..256 chunks
+  int tpc = kThreads;                                       // threads per chunk
+  while (tpc * W > kThreads) tpc >>= 1;
+  const int cw = tid / tpc, sub = tid % tpc;                // this thread's chunk
+  const bool has_chunk = cw < W;
+  const int64_t slot = row * p.fuse.nchunk + (has_chunk ? cw : 0);
+  const uint32_t *tab = p.fuse.tab + slot * kFuseTabCap;
+  const uint32_t *lst = p.fuse.list + slot * kFuseChunk;
+  auto bin_of = [](uint32_t v) { return v >> 20; };
+  auto cnt_of = [](uint32_t v) { return (v & 1023u) + 1u; };
+
+  // 1. row histogram.  Table entries sub, sub + tpc, ... of this thread's
+  // chunk; the first kFuseBatch stay in registers for step 2.
+  uint32_t z = has_chunk ? p.fuse.nz[slot] : 0u;
+  z = z < (uint32_t)kFuseTabCap ? z : (uint32_t)kFuseTabCap;
+  for (int i = tid; i < kFuseBins; i += kThreads) fs.hist[i] = 0u;
+  uint32_t t0[kFuseBatch];
+#pragma unroll
+  for (int u = 0; u < kFuseBatch; ++u) {
+    const uint32_t e = sub + u * tpc;
+    t0[u] = tab[e < z ? e : 0u];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kFuseBatch; ++u)
+    if (sub + u * tpc < z) atomicAdd(&fs.hist[bin_of(t0[u])], cnt_of(t0[u]));
+  for (uint32_t e0 = sub + kFuseBatch * tpc; e0 < z; e0 += kFuseBatch * tpc) {
+    uint32_t v[kFuseBatch];
+#pragma unroll
+    for (int u = 0; u < kFuseBatch; ++u) {
+      const uint32_t e = e0 + u * tpc;
+      v[u] = tab[e < z ? e : 0u];
+    }
+#pragma unroll
+    for (int u = 0; u < kFuseBatch; ++u)
+      if (e0 + u * tpc < z) atomicAdd(&fs.hist[bin_of(v[u])], cnt_of(v[u]));
+  }
+  if (tid < W) {
+    fs.na[tid] = 0u;
+    fs.ne[tid] = 0u;
+  }
+  __syncthreads();
+  {
+    // thread t owns bins 4095 - 8t .. 4088 - 8t (descending)
+    constexpr int kPer = kFuseBins / kThreads;
+    uint32_t hc[kPer], hs = 0u;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      hc[i] = fs.hist[kFuseBins - 1 - kPer * tid - i];
+      hs += hc[i];
+    }
+    uint32_t tot;
+    uint32_t cum = block_exclusive_scan(hs, sh, tot);
+    if (cum < (uint32_t)k && cum + hs >= (uint32_t)k) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        if (cum < (uint32_t)k && cum + hc[i] >= (uint32_t)k) {
+          sh.bcast[0] = (uint32_t)(kFuseBins - 1 - kPer * tid - i);
+          sh.bcast[1] = cum;
+          sh.bcast[2] = hc[i];
+        }
+        cum += hc[i];
+      }
+    }
+    __syncthreads();
+  }
+  const uint32_t B1 = sh.bcast[0], A = sh.bcast[1], E = sh.bcast[2];
+
+  // 2. per chunk: keys above B1 (na) and in B1 (ne), where they go, and the
+  // list prefixes themselves
+  auto count_entry = [&](uint32_t v) {
+    const uint32_t b = bin_of(v);
+    if (b > B1) atomicAdd(&fs.na[cw], cnt_of(v));
+    else if (b == B1) fs.ne[cw] = cnt_of(v);
+  };
+#pragma unroll
+  for (int u = 0; u < kFuseBatch; ++u)
+    if (sub + u * tpc < z) count_entry(t0[u]);
+  for (uint32_t e0 = sub + kFuseBatch * tpc; e0 < z; e0 += kFuseBatch * tpc) {
+    uint32_t v[kFuseBatch];
+#pragma unroll
+    for (int u = 0; u < kFuseBatch; ++u) {
+      const uint32_t e = e0 + u * tpc;
+      v[u] = tab[e < z ? e : 0u];
+    }
+#pragma unroll
+    for (int u = 0; u < kFuseBatch; ++u)
+      if (e0 + u * tpc < z) count_entry(v[u]);
+  }
+  __syncthreads();
+  {
+    // A < k <= 4096 fits 13 bits, E <= n <= 2^18 the 19 above them
+    const uint32_t pk = tid < W ? (fs.ne[tid] << 13 | fs.na[tid]) : 0u;
+    uint32_t ptot;
+    const uint32_t pex = block_exclusive_scan(pk, sh, ptot);
+    if (tid < W) {
+      fs.offa[tid] = pex & 0x1FFFu;
+      fs.offe[tid] = pex >> 13;
+    }
+    __syncthreads();
+  }
+  const bool e_in_lds = E <= (uint32_t)kCap;
+  {
+    const uint32_t na = has_chunk ? fs.na[cw] : 0u;
+    const uint32_t take = has_chunk ? na + (e_in_lds ? fs.ne[cw] : 0u) : 0u;
+    const uint32_t oa = has_chunk ? fs.offa[cw] : 0u, oe = has_chunk ? fs.offe[cw] : 0u;
+    for (uint32_t e0 = sub; e0 < take; e0 += kFuseBatch * tpc) {
+      uint32_t v[kFuseBatch];
+#pragma unroll
+      for (int u = 0; u < kFuseBatch; ++u) {
+        const uint32_t e = e0 + u * tpc;
+        v[u] = lst[e < take ? e : 0u];
+      }
+#pragma unroll
+      for (int u = 0; u < kFuseBatch; ++u) {
+        const uint32_t e = e0 + u * tpc;
+        if (e < take) {
+          const uint32_t q = (uint32_t)cw * kFuseChunk + (v[u] & 1023u);
+          if (e < na) {
+            fs.above[oa + e] = q;
+          } else {
+            sh.keys[oe + e - na] = B1 << 20 | v[u] >> 10;
+            sh.pos[oe + e - na] = q;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // The i-th key of B1 (in chunk order) and its position: from LDS, or from
+  // the lists when there are too many of them for LDS.
+  auto b1_entry = [&](uint32_t i, uint32_t &key, uint32_t &q) {
+    if (e_in_lds) {
+      key = sh.keys[i];
+      q = sh.pos[i];
+      return;
+    }
+    int lo = 0, hi = W - 1;                       // the last chunk whose offe is <= i
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (fs.offe[mid] <= i) lo = mid;
+      else hi = mid - 1;
+    }
+    const uint32_t v = p.fuse.list[(row * p.fuse.nchunk + lo) * kFuseChunk + fs.na[lo] + (i - fs.offe[lo])];
+    key = B1 << 20 | v >> 10;
+    q = (uint32_t)lo * kFuseChunk + (v & 1023u);
+  };
+
+  // 3. threshold among the keys of B1
+  uint32_t thr, n_above;
+  radix_select([&](int64_t i) { uint32_t key, q; b1_entry((uint32_t)i, key, q); return key; }, E,
+               (uint32_t)k - A, sh, thr, n_above);
+  const uint32_t need_eq = (uint32_t)k - A - n_above;
+
+  // 4. position bitmaps, ties limited to the lowest positions, emission.
+  // Thread t owns words [t * wpt, t * wpt + wpt).
+  const int nw = (int)((n + 31) >> 5);
+  const int wpt = (nw + kThreads - 1) / kThreads;  // <= kFuseWords / kThreads
+  for (int i = tid; i < nw; i += kThreads) {
+    fs.bm.sel[i] = 0u;
+    fs.bm.eq[i] = 0u;
+  }
+  __syncthreads();
+  for (uint32_t i = tid; i < A; i += kThreads) {
+    const uint32_t q = fs.above[i];
+    atomicOr(&fs.bm.sel[q >> 5], 1u << (q & 31));
+  }
+  for (uint32_t i = tid; i < E; i += kThreads) {
+    uint32_t key, q;
+    b1_entry(i, key, q);
+    if (key > thr) atomicOr(&fs.bm.sel[q >> 5], 1u << (q & 31));
+    else if (key == thr) atomicOr(&fs.bm.eq[q >> 5], 1u << (q & 31));
+  }
+  __syncthreads();
+  const int w0 = wpt * tid;
+  uint32_t ec = 0u;
+  for (int u = 0; u < wpt; ++u) ec += w0 + u < nw ? (uint32_t)__popc(fs.bm.eq[w0 + u]) : 0u;
+  uint32_t etot;
+  uint32_t eb = block_exclusive_scan(ec, sh, etot);
+  uint32_t sc = 0u;
+  for (int u = 0; u < wpt; ++u) {
+    if (w0 + u < nw) {
+      const uint32_t x = fs.bm.eq[w0 + u], c = (uint32_t)__popc(x);
+      const uint32_t keep = need_eq > eb ? (need_eq - eb < c ? need_eq - eb : c) : 0u;
+      uint32_t y = fs.bm.sel[w0 + u];
+      if (keep) y |= keep == c ? x : lowest_set_bits(x, keep);
+      fs.bm.sel[w0 + u] = y;
+      sc += (uint32_t)__popc(y);
+      eb += c;
+    }
+  }
+  uint32_t stot;
+  uint32_t at = block_exclusive_scan(sc, sh, stot);
+  for (int u = 0; u < wpt; ++u) {
+    if (w0 + u < nw) {
+      uint32_t x = fs.bm.sel[w0 + u];
+      while (x != 0u) {
+        if (at < (uint32_t)k) out[at] = (int32_t)(32 * (w0 + u) + __builtin_ctz(x));
+        ++at;
+        x &= x - 1u;
+      }
+    }
+  }
+}
 }  // namespace
 
 namespace {
@@ -585,6 +858,23 @@ size_t split_bytes(const TopkArgs &a, int32_t nseg) {
 size_t topk_workspace_bytes(const TopkArgs &a) {
   int32_t seg_len, nseg;
   return split_geometry(a, seg_len, nseg) ? split_bytes(a, nseg) : 0;
+}
+
+bool fuse_eligible(const SeqLayout &seq) {
+  return decode_indexer(seq) && seq.total_q > 0 && seq.max_kv_len > 0 && seq.max_kv_len <= kFuseMaxLen;
+}
+
+size_t fuse_workspace_bytes(const SeqLayout &seq) {
+  if (!fuse_eligible(seq)) return 0;
+  const size_t slots = (size_t)seq.total_q * (size_t)((seq.max_kv_len + kFuseChunk - 1) / kFuseChunk);
+  auto r256 = [](size_t x) { return (x + 255) / 256 * 256; };
+  return r256(slots * kFuseTabCap * 4) + r256(slots * 4) + slots * kFuseChunk * 4;
+}
+
+hipError_t launch_topk_fused(const TopkArgs &a, hipStream_t stream) {
+  if (a.seq.total_q == 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_fused_kernel, dim3((unsigned)a.seq.total_q), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
 }
 
 hipError_t launch_topk(const TopkArgs &a, hipStream_t stream) {

@@ -236,6 +236,25 @@ def test_forward_noalloc_refuses_problems_beyond_its_scratch():
     assert lib.dsa_workspace_bytes(ctypes.byref(dec), binding.WS_FORWARD) <= binding.NOALLOC_SCRATCH_BYTES
 
 
+def test_forward_fused_serves_decode_shapes_only():
+    """dsa_forward_fused needs at most two query rows per sequence and rows of
+    at most 262144 keys; anything else is refused before a launch."""
+    lib = binding.load_library()
+    pre = _problem()                                   # a 4096-row prefill
+    assert lib.dsa_workspace_bytes(ctypes.byref(pre), binding.WS_FORWARD_FUSED) == ctypes.c_size_t(-1).value
+    assert lib.dsa_forward_fused(ctypes.byref(pre), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 None, None, FAKE, 1 << 40, None) == binding.DSA_ERR_UNSUPPORTED
+    assert "two query rows" in _msg()
+    dec = _problem(batch=64, total_q=64, max_q_len=1, total_kv=64 * 131072, max_kv_len=131072)
+    need = lib.dsa_workspace_bytes(ctypes.byref(dec), binding.WS_FORWARD_FUSED)
+    assert 0 < need < lib.dsa_workspace_bytes(ctypes.byref(dec), binding.WS_FORWARD) + (80 << 20)
+    assert lib.dsa_forward_fused(ctypes.byref(dec), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 None, None, FAKE, need - 1, None) == binding.DSA_ERR_WORKSPACE
+    long_row = _problem(batch=1, total_q=1, max_q_len=1, total_kv=(1 << 18) + 1, max_kv_len=(1 << 18) + 1)
+    assert lib.dsa_workspace_bytes(ctypes.byref(long_row), binding.WS_FORWARD_FUSED) == \
+        ctypes.c_size_t(-1).value
+
+
 def _align(p, lse=FAKE, scores=FAKE, idx=FAKE, loss=FAKE, grad=FAKE, ld=4096, ld_grad=2048):
     lib = binding.load_library()
     return lib.dsa_indexer_align_loss(ctypes.byref(p), FAKE, FAKE, lse, scores, ld, idx, loss, grad,
