@@ -32,6 +32,7 @@ namespace {
 constexpr int kWaves = 4;          // waves per workgroup
 constexpr int kKeyTile = 64;       // keys per LDS tile in the prefill kernel
 constexpr int kRowBytes = 128;     // one key row in LDS (d_I padded to 128)
+constexpr int64_t kL2Bytes = 4 << 20;   // L2 per XCD
 
 // LDS position of 16-byte chunk j of key n inside a key tile.  Chunk slots
 // are XOR-swizzled by (n >> 1) & 7 so the 16 lanes of a row reading the same
@@ -169,7 +170,7 @@ __device__ __forceinline__ float reduce_four_blocks(float p0, float p1, float p2
 // (tiles start at multiples of 64, blocks hold a multiple of 64 rows).
 template <int HB, int QW, bool kPaged>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
-void indexer_prefill_kernel(IndexerArgs p, int key_split) {
+void indexer_prefill_kernel(IndexerArgs p, int key_split, int xcd_splits) {
   constexpr int QT = kWaves * QW;
   __shared__ __attribute__((aligned(16))) uint8_t ktile[2][kKeyTile * kRowBytes];
   __shared__ __attribute__((aligned(16))) uint8_t linq[kWaves][QW * kLinPieces * 128];
@@ -178,18 +179,22 @@ void indexer_prefill_kernel(IndexerArgs p, int key_split) {
   const int sb = (int)__builtin_amdgcn_workgroup_id_z();
   const SeqInfo s = load_seq(p.seq, sb);
   const int64_t qlen = s.q1 - s.q0;
-  const int64_t row_begin = (int64_t)__builtin_amdgcn_workgroup_id_y() * QT;
+  // Without XCD-bound splits the query tiles go out last first: the causal
+  // triangle makes them the longest, and the short ones then fill the tail.
+  const int wy = (int)__builtin_amdgcn_workgroup_id_y();
+  const int qtile = __builtin_amdgcn_readfirstlane(xcd_splits ? wy : (int)gridDim.y - 1 - wy);
+  const int64_t row_begin = (int64_t)qtile * QT;
   if (row_begin >= qlen || s.kvlen <= 0) return;
   const int64_t rows_here = qlen - row_begin < QT ? qlen - row_begin : QT;
   const int64_t last_pos = row_pos(s, s.q0 + row_begin + rows_here - 1);
   // Positions inside one sequence fit in int32 (the offsets are int32).
-  // Workgroup x runs on XCD x % 8 (dispatch is round-robin over the eight
-  // XCDs, and the split count is a multiple of 8), so each XCD keeps a fixed
-  // set of key splits in its L2.  The splits go to the XCDs in snake order
+  // With xcd_splits, workgroup x runs on XCD x % 8 (dispatch is round-robin
+  // over the eight XCDs, and the split count is a multiple of 8), so each XCD
+  // keeps a fixed set of key splits in its L2.  The splits go to the XCDs in snake order
   // (x, 15 - x, 16 + x, 31 - x, ...): under the causal triangle later splits
   // have less work, and the pairs even it out across the XCDs.
   const int sx = (int)__builtin_amdgcn_workgroup_id_x(), sxcd = sx & 7, sj = sx >> 3;
-  const int key_begin = ((sj & 1) ? 8 * sj + 7 - sxcd : 8 * sj + sxcd) * key_split;
+  const int key_begin = (!xcd_splits ? sx : ((sj & 1) ? 8 * sj + 7 - sxcd : 8 * sj + sxcd)) * key_split;
   if (key_begin > last_pos) return;
   const int key_end = key_begin + key_split < last_pos + 1 ? key_begin + key_split : (int)last_pos + 1;
   const int kvlen = (int)s.kvlen;
@@ -525,29 +530,45 @@ template <int HB, int QW>
 hipError_t launch_prefill(const IndexerArgs &a, hipStream_t stream) {
   constexpr int QT = kWaves * QW;
   const int64_t qtiles = (a.seq.max_q_len + QT - 1) / QT;
-  // Key splits: 8m of them, m >= 2, of equal length (a multiple of 64), so
-  // that every XCD gets the same share of the keys.  m is the smallest that
-  // leaves about 6K workgroups with work (several rounds of the 256 CUs x 2-3
-  // resident workgroups, so the causal tail evens out), with splits of at
-  // least 256 keys; fewer, longer splits load the queries and build their
-  // linear operand less often.  Work estimate: the longest sequence's queries
-  // sit at its last max_q_len positions.
-  const double first_pos = (double)(a.seq.max_kv_len - a.seq.max_q_len);
+  const int64_t kv = a.seq.max_kv_len;
+  // Work estimate: the longest sequence's queries sit at its last max_q_len
+  // positions; busy_blocks(sp) counts the workgroups with causal keys.
+  const double first_pos = (double)(kv - a.seq.max_q_len);
   auto busy_blocks = [&](int64_t sp) {
     const double t = (double)qtiles;
     return ((t * first_pos + QT * t * (t + 1) / 2) / sp + t / 2) * a.seq.batch;
   };
-  const int64_t kv = a.seq.max_kv_len;
-  auto split_of = [&](int64_t m) { return ((kv + 8 * m - 1) / (8 * m) + 63) / 64 * 64; };
-  int64_t m = 2;
-  while (split_of(m + 1) >= 256 && busy_blocks(split_of(m)) < 6144) ++m;
-  const int64_t split = split_of(m);
-  const int64_t nsplit = 8 * m;
+  auto split_of = [&](int64_t m) { return ((kv + m - 1) / m + 63) / 64 * 64; };
+  int64_t nsplit, split;
+  int xcd_splits;
+  if (kv * a.idx_dim <= (int64_t)kL2Bytes) {
+    // The longest sequence's keys fit one XCD's L2, so every XCD can hold all
+    // of them: as few splits as leave 1024 or more workgroups with keys (the
+    // queries are loaded, and their linear operand built, once per split).
+    nsplit = 1;
+    while (nsplit < 8 && busy_blocks(split_of(nsplit)) < 1024) nsplit *= 2;
+    split = split_of(nsplit);
+    xcd_splits = 0;
+  } else {
+    // Key splits: 8m of them, m >= 2, of equal length (a multiple of 64), so
+    // that every XCD gets the same share of the keys.  m is the smallest that
+    // leaves about 6K workgroups with work (several rounds of the 256 CUs x
+    // 2-3 resident workgroups, so the causal tail evens out), with splits of
+    // at least 256 keys; fewer, longer splits load the queries and build
+    // their linear operand less often.
+    int64_t m = 2;
+    while (split_of(8 * (m + 1)) >= 256 && busy_blocks(split_of(8 * m)) < 6144) ++m;
+    nsplit = 8 * m;
+    split = split_of(nsplit);
+    xcd_splits = 1;
+  }
   dim3 grid((unsigned)nsplit, (unsigned)qtiles, (unsigned)a.seq.batch);
   if (a.pg.table != nullptr)
-    hipLaunchKernelGGL((indexer_prefill_kernel<HB, QW, true>), grid, dim3(256), 0, stream, a, (int)split);
+    hipLaunchKernelGGL((indexer_prefill_kernel<HB, QW, true>), grid, dim3(256), 0, stream, a, (int)split,
+                       xcd_splits);
   else
-    hipLaunchKernelGGL((indexer_prefill_kernel<HB, QW, false>), grid, dim3(256), 0, stream, a, (int)split);
+    hipLaunchKernelGGL((indexer_prefill_kernel<HB, QW, false>), grid, dim3(256), 0, stream, a, (int)split,
+                       xcd_splits);
   return hipGetLastError();
 }
 
