@@ -37,6 +37,13 @@
  *   Validation runs on the host before anything is enqueued: on a non-OK
  *   status nothing was launched and dsa_last_error() describes the problem.
  *   Faults inside kernels surface at the caller's next synchronisation.
+ * - Debug builds (libdsa_debug.so, compiled with DSA_DEBUG): every call also
+ *   synchronises its stream, copies the offset arrays (and a paged cache's
+ *   block table) to the host and checks them -- offsets from 0 to the totals,
+ *   no sequence longer than the maxima, q_pos0[b] + q_len_b <= kv_len_b,
+ *   table entries of used blocks inside the cache -- returning
+ *   DSA_ERR_INVALID_ARGUMENT before any launch when they are inconsistent.
+ *   dsa_version() then ends in " debug".
  */
 #ifndef DSA_H_
 #define DSA_H_

@@ -85,42 +85,46 @@ def load_library():
     """Load libdsa.so once and declare its signatures."""
     global _lib
     with _lock:
-        if _lib is not None:
-            return _lib
-        if not os.path.exists(_LIB_PATH):
-            raise DsaLibraryError(
-                f"{_LIB_PATH} is missing: build it with `python -m sparse_attention_18_amd.build`")
-        try:
-            lib = ctypes.CDLL(_LIB_PATH)
-        except OSError as e:
-            raise DsaLibraryError(f"cannot load {_LIB_PATH}: {e}") from e
-        P = ctypes.POINTER(DsaProblem)
-        vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
-        lib.dsa_indexer_scores.argtypes = [P, vp, vp, vp, vp, vp, vp, i64, vp]
-        lib.dsa_topk.argtypes = [P, vp, i64, vp, vp, sz, vp]
-        lib.dsa_sparse_attn.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
-        lib.dsa_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-        G = ctypes.POINTER(DsaPagedKV)
-        lib.dsa_indexer_scores_paged.argtypes = [P, G, vp, vp, vp, vp, vp, vp, i64, vp]
-        lib.dsa_sparse_attn_paged.argtypes = [P, G, vp, vp, vp, vp, vp, vp, sz, vp]
-        lib.dsa_forward_paged.argtypes = [P, G, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-        lib.dsa_indexer_align_loss.argtypes = [P, vp, vp, vp, vp, i64, vp, vp, vp, i64, vp]
-        lib.dsa_indexer_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]
-        lib.dsa_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
-        lib.dsa_forward_fused.argtypes = [P, G, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
-        for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward",
-                     "dsa_indexer_scores_paged", "dsa_sparse_attn_paged", "dsa_forward_paged",
-                     "dsa_indexer_align_loss", "dsa_indexer_backward", "dsa_forward_noalloc",
-                     "dsa_forward_fused"):
-            getattr(lib, name).restype = ctypes.c_int
-        lib.dsa_workspace_bytes.argtypes = [P, ctypes.c_int]
-        lib.dsa_workspace_bytes.restype = sz
-        lib.dsa_last_error.argtypes = []
-        lib.dsa_last_error.restype = ctypes.c_char_p
-        lib.dsa_version.argtypes = []
-        lib.dsa_version.restype = ctypes.c_char_p
-        _lib = lib
-        return lib
+        if _lib is None:
+            _lib = open_library(_LIB_PATH)
+        return _lib
+
+
+def open_library(path: str):
+    """Load a build of the library at `path` (libdsa.so or one of its
+    variants, e.g. libdsa_debug.so) and declare its signatures."""
+    if not os.path.exists(path):
+        raise DsaLibraryError(f"{path} is missing: build it with `python -m sparse_attention_18_amd.build`")
+    try:
+        lib = ctypes.CDLL(path)
+    except OSError as e:
+        raise DsaLibraryError(f"cannot load {path}: {e}") from e
+    P = ctypes.POINTER(DsaProblem)
+    vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+    lib.dsa_indexer_scores.argtypes = [P, vp, vp, vp, vp, vp, vp, i64, vp]
+    lib.dsa_topk.argtypes = [P, vp, i64, vp, vp, sz, vp]
+    lib.dsa_sparse_attn.argtypes = [P, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dsa_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    G = ctypes.POINTER(DsaPagedKV)
+    lib.dsa_indexer_scores_paged.argtypes = [P, G, vp, vp, vp, vp, vp, vp, i64, vp]
+    lib.dsa_sparse_attn_paged.argtypes = [P, G, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dsa_forward_paged.argtypes = [P, G, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dsa_indexer_align_loss.argtypes = [P, vp, vp, vp, vp, i64, vp, vp, vp, i64, vp]
+    lib.dsa_indexer_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]
+    lib.dsa_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.dsa_forward_fused.argtypes = [P, G, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward",
+                 "dsa_indexer_scores_paged", "dsa_sparse_attn_paged", "dsa_forward_paged",
+                 "dsa_indexer_align_loss", "dsa_indexer_backward", "dsa_forward_noalloc",
+                 "dsa_forward_fused"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.dsa_workspace_bytes.argtypes = [P, ctypes.c_int]
+    lib.dsa_workspace_bytes.restype = sz
+    lib.dsa_last_error.argtypes = []
+    lib.dsa_last_error.restype = ctypes.c_char_p
+    lib.dsa_version.argtypes = []
+    lib.dsa_version.restype = ctypes.c_char_p
+    return lib
 
 
 def _check(status: int):

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/dsa.h"
 #include "launch.h"
@@ -159,6 +160,61 @@ dsa_status hip_status(hipError_t e, const char *what) {
   return fail(DSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+#ifdef DSA_DEBUG
+// Debug builds: the device arrays the kernels index with -- the sequence
+// offsets and first positions, and a paged cache's block table -- are copied
+// to the host (after synchronizing the stream) and checked before anything
+// is launched.  Release builds cannot check them and only clamp every index
+// derived from them inside the kernels.
+dsa_status debug_check_layout(const dsa_problem *p, const dsa_paged_kv *pg, void *stream) {
+  const int B = p->batch;
+  std::vector<int32_t> qo(B + 1), ko(B + 1), p0(B);
+  DSA_TRY(hip_status(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "debug: stream synchronize"));
+  DSA_TRY(hip_status(hipMemcpy(qo.data(), p->q_offsets, qo.size() * 4, hipMemcpyDeviceToHost),
+                     "debug: copying q_offsets"));
+  DSA_TRY(hip_status(hipMemcpy(ko.data(), p->kv_offsets, ko.size() * 4, hipMemcpyDeviceToHost),
+                     "debug: copying kv_offsets"));
+  DSA_TRY(hip_status(hipMemcpy(p0.data(), p->q_pos0, p0.size() * 4, hipMemcpyDeviceToHost),
+                     "debug: copying q_pos0"));
+  DSA_CHECK(qo[0] == 0 && qo[B] == p->total_q, DSA_ERR_INVALID_ARGUMENT,
+            "debug: q_offsets must run from 0 to total_q (%lld), found %d .. %d",
+            (long long)p->total_q, qo[0], qo[B]);
+  DSA_CHECK(ko[0] == 0 && ko[B] == p->total_kv, DSA_ERR_INVALID_ARGUMENT,
+            "debug: kv_offsets must run from 0 to total_kv (%lld), found %d .. %d",
+            (long long)p->total_kv, ko[0], ko[B]);
+  for (int b = 0; b < B; ++b) {
+    const int64_t ql = (int64_t)qo[b + 1] - qo[b], kl = (int64_t)ko[b + 1] - ko[b];
+    DSA_CHECK(ql >= 0 && ql <= p->max_q_len, DSA_ERR_INVALID_ARGUMENT,
+              "debug: sequence %d has %lld query rows (max_q_len %lld)", b, (long long)ql,
+              (long long)p->max_q_len);
+    DSA_CHECK(kl >= 0 && kl <= p->max_kv_len, DSA_ERR_INVALID_ARGUMENT,
+              "debug: sequence %d has %lld keys (max_kv_len %lld)", b, (long long)kl,
+              (long long)p->max_kv_len);
+    DSA_CHECK(p0[b] >= 0 && p0[b] + ql <= kl, DSA_ERR_INVALID_ARGUMENT,
+              "debug: sequence %d: q_pos0 (%d) + query rows (%lld) exceeds its keys (%lld)", b, p0[b],
+              (long long)ql, (long long)kl);
+  }
+  if (pg != nullptr) {
+    std::vector<int32_t> tab((size_t)B * pg->max_blocks);
+    DSA_TRY(hip_status(hipMemcpy(tab.data(), pg->block_table, tab.size() * 4, hipMemcpyDeviceToHost),
+                       "debug: copying block_table"));
+    for (int b = 0; b < B; ++b) {
+      const int64_t used = ((int64_t)ko[b + 1] - ko[b] + pg->block_size - 1) / pg->block_size;
+      for (int64_t j = 0; j < used; ++j) {
+        const int32_t v = tab[(size_t)b * pg->max_blocks + j];
+        DSA_CHECK(v >= 0 && v < pg->num_blocks, DSA_ERR_INVALID_ARGUMENT,
+                  "debug: block_table[%d][%lld] = %d is outside [0, %lld)", b, (long long)j, v,
+                  (long long)pg->num_blocks);
+      }
+    }
+  }
+  return DSA_OK;
+}
+#define DSA_DEBUG_CHECK(p, pg, stream) DSA_TRY(debug_check_layout((p), (pg), (stream)))
+#else
+#define DSA_DEBUG_CHECK(p, pg, stream) ((void)0)
+#endif
+
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Leading dimension of the scores matrix dsa_forward keeps in its workspace.
@@ -301,7 +357,11 @@ extern "C" {
 
 const char *dsa_last_error(void) { return g_error.c_str(); }
 
+#ifdef DSA_DEBUG
+const char *dsa_version(void) { return "dsa 0.1.0 gfx950 debug"; }
+#else
 const char *dsa_version(void) { return "dsa 0.1.0 gfx950"; }
+#endif
 
 size_t dsa_workspace_bytes(const dsa_problem *p, int which) {
   if (check_problem(p) != DSA_OK) return (size_t)-1;
@@ -334,6 +394,7 @@ dsa_status indexer_impl(const dsa_problem *p, const dsa_paged_kv *pg, const uint
   DSA_TRY(check_ld(p, ld_scores));
   DSA_TRY(check_indexer_ptrs(p, q_fp8, q_scale, w, k_fp8, k_scale));
   DSA_TRY(check_ptr(scores, p->total_q > 0, "scores"));
+  DSA_DEBUG_CHECK(p, pg, stream);
   return hip_status(dsa::launch_indexer(indexer_args(p, q_fp8, q_scale, w, k_fp8, k_scale,
                                                      scores, ld_scores, pg),
                                         static_cast<hipStream_t>(stream)),
@@ -369,6 +430,7 @@ dsa_status dsa_topk(const dsa_problem *p, const float *scores, int64_t ld_scores
             "top-k workspace needs %zu bytes (got %zu)", need, workspace_bytes);
   DSA_CHECK(need == 0 || aligned16(workspace), DSA_ERR_INVALID_ARGUMENT,
             "workspace must be 16-byte aligned");
+  DSA_DEBUG_CHECK(p, nullptr, stream);
   return hip_status(dsa::launch_topk(topk_args(p, scores, ld_scores, topk_idx, workspace,
                                                workspace_bytes),
                                      static_cast<hipStream_t>(stream)),
@@ -392,6 +454,7 @@ dsa_status attn_impl(const dsa_problem *p, const dsa_paged_kv *pg, const uint16_
             "attention workspace needs %zu bytes (got %zu)", need, workspace_bytes);
   DSA_CHECK(need == 0 || aligned16(workspace), DSA_ERR_INVALID_ARGUMENT,
             "workspace must be 16-byte aligned");
+  DSA_DEBUG_CHECK(p, pg, stream);
   return hip_status(dsa::launch_sparse_attn(attn_args(p, q, kv, topk_idx, out, lse, workspace,
                                                       workspace_bytes, pg),
                                             static_cast<hipStream_t>(stream)),
@@ -417,6 +480,7 @@ dsa_status forward_impl(const dsa_problem *p, const dsa_paged_kv *pg, const uint
   DSA_CHECK(workspace_bytes >= ws.total && workspace != nullptr, DSA_ERR_WORKSPACE,
             "forward workspace needs %zu bytes (got %zu)", ws.total, workspace_bytes);
   DSA_CHECK(aligned16(workspace), DSA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  DSA_DEBUG_CHECK(p, pg, stream);
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t *base = static_cast<uint8_t *>(workspace);
   float *scores = reinterpret_cast<float *>(base);
@@ -507,6 +571,7 @@ dsa_status align_impl(const dsa_problem *p, const uint16_t *q, const uint16_t *k
             topk_idx != nullptr ? "topk" : "max_kv_len", (long long)need);
   DSA_CHECK(!hq || ld_grad <= INT64_MAX / 4 / p->total_q, DSA_ERR_INVALID_ARGUMENT,
             "grad matrix size overflows");
+  DSA_DEBUG_CHECK(p, nullptr, stream);
   dsa::AlignArgs a;
   a.seq = layout_of(p);
   a.q = q;
@@ -572,6 +637,7 @@ dsa_status indexer_bwd_impl(const dsa_problem *p, const uint8_t *q_fp8, const fl
     DSA_CHECK(aligned16(workspace), DSA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
     DSA_CHECK(p->total_kv / 64 < INT32_MAX, DSA_ERR_UNSUPPORTED, "total_kv too large for the workspace path");
   }
+  DSA_DEBUG_CHECK(p, nullptr, stream);
   dsa::IndexerBwdArgs a{};
   a.seq = layout_of(p);
   a.q_fp8 = q_fp8;
