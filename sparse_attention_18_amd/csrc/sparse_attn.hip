@@ -59,16 +59,25 @@ constexpr int kMaxSplits = 4;                // workgroups per token in the spli
 // S^T accumulation MFMAs, pinned to VGPRs.  The P.V accumulators fill all
 // 256 AGPRs; left to itself the compiler puts this accumulator in AGPRs too
 // and spills part of O.  The chain's dependent MFMAs are interlocked by the
-// hardware; the VALU reads of the result follow qk_drain().
+// hardware; the chain ends in qk_mfma_last_drain, which waits for the result.
 __device__ __forceinline__ void qk_mfma_first(v16f &acc, const v4i &a, const v8bf &b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
 }
 __device__ __forceinline__ void qk_mfma(v16f &acc, const v4i &a, const v8bf &b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
-// Wait states between the last S^T MFMA (written through asm, so invisible
-// to the compiler's hazard tracking) and the first VALU read of its result.
-__device__ __forceinline__ void qk_drain() { asm volatile("s_nop 15\n\ts_nop 15" ::: "memory"); }
+// The last link of the chain, with the wait for its result, in one asm
+// statement: the compiler takes an asm's result as ready and its sources as
+// free once it issues, so an instruction placed between a separate last link
+// and its wait could read sums still in flight (a copy of the accumulator)
+// or overwrite C, which the matrix core reads late in the instruction.  The
+// output is not tied to the accumulator, so that no copy is needed after it.
+__device__ __forceinline__ v16f qk_mfma_last_drain(const v16f &acc, const v4i &a, const v8bf &b) {
+  v16f r;
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %3\n\ts_nop 15\n\ts_nop 15"
+               : "=&v"(r) : "v"(a), "v"(b), "v"(acc) : "memory");
+  return r;
+}
 
 template <int NW, bool kPaged>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -276,7 +285,8 @@ void mla_sparse_attn_kernel(AttnArgs p) {
 #pragma unroll
       for (int i = 0; i < KS; ++i) {
         if (i == 0) qk_mfma_first(sc, a[0], qb[0]);
-        else qk_mfma(sc, a[i % LA], qb[i]);
+        else if (i + 1 < KS) qk_mfma(sc, a[i % LA], qb[i]);
+        else sc = qk_mfma_last_drain(sc, a[i % LA], qb[i]);
         if (i + LA < KS) a[i % LA] = *reinterpret_cast<const DSA_LDS v4i *>(tbq + qk_off(i + LA));
         if (i < NPV) {
           const int g = i / NW, nb = i % NW, hf = g / MB, u = g % MB;
@@ -291,7 +301,6 @@ void mla_sparse_attn_kernel(AttnArgs p) {
             if (i == w * KS / kWindows) gather_window(src, gbase, w);
         __builtin_amdgcn_sched_barrier(0);
       }
-      qk_drain();
       return sc;
     };
 
