@@ -25,6 +25,10 @@ What it computes, stage by stage, in the order the pages give:
    gather, softmax-weighted sum): MQA/MLA over the selected rows only.  All
    heads of a token share one latent KV row per key; the key is the whole
    row (latent + rope), the value its latent part.
+3b. Prefill mode.  The threadnavigator.com thread (first tweet): separate
+   attention modes for prefill and decode.  Read as MLA's per-head form:
+   each head has its own key (decompressed part + shared rotary part) and
+   value, over the same selected set.
 4. Indexer alignment loss (training).  ivugangingo.com article, section
    "DeepSeek sparse attention pre-training continues": the indexer is trained
    with a KL loss towards the attention's distribution, over all causal keys
@@ -150,6 +154,53 @@ def sparse_attention_row(q_row, kv, idx, scale: float, d_latent: int):
     out = (e @ rows[:, :d_latent]) / den
     lse = mx[:, 0] + np.log(den[:, 0])
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# Stage 3, prefill mode: per-head keys and values
+# ---------------------------------------------------------------------------
+# The threadnavigator.com thread on DeepSeek-V3.2 (first tweet) notes that the
+# model runs different attention modes for disaggregated prefill and decode.
+# The pages give no shapes.  The reading used here is MLA's two forms of the
+# same attention: the form of stage 3 (queries taken into the latent space,
+# one shared latent + rope row per key) serves decode; for prefill every head
+# has its own key -- a part decompressed from the latent, followed by the
+# rotary key that all heads share -- and its own value, and the query of a
+# head is as wide as its key.  The selector's set restricts the keys as a
+# mask: each valid position of a row counts once.
+def mha_attention_row(q_row, k_nope, k_rope, v, idx, scale: float, kv_len: int):
+    """Prefill-mode attention of one token's H heads over its selected keys.
+
+    q_row [H, dn + dr]; k_nope [S, H, dn]; k_rope [S, dr]; v [S, H, dv]
+    (float64, rows = key positions of the token's sequence); idx [k]
+    positions.  sel = the distinct entries of idx in [0, kv_len), ascending.
+    logits[h, i] = scale * (q_row[h, :dn] . k_nope[sel_i, h] + q_row[h, dn:] . k_rope[sel_i]);
+    out[h] = sum_i softmax_i(logits[h]) * v[sel_i, h]; lse[h] = log sum_i exp(logits[h, i]).
+    Returns (out [H, dv], lse [H]); with nothing selected, 0 and -inf.
+    """
+    idx = np.asarray(idx)
+    sel = np.unique(idx[(idx >= 0) & (idx < kv_len)])
+    H, dn = q_row.shape[0], k_nope.shape[2]
+    if sel.size == 0:
+        return np.zeros((H, v.shape[2])), np.full(H, -np.inf)
+    out = np.zeros((H, v.shape[2]))
+    lse = np.zeros(H)
+    for h in range(H):
+        keys = np.concatenate([k_nope[sel, h, :], k_rope[sel]], axis=1)   # [m, dn + dr]
+        logits = scale * (keys @ q_row[h])
+        mx = logits.max()
+        e = np.exp(logits - mx)
+        out[h] = (e @ v[sel, h, :]) / e.sum()
+        lse[h] = mx + np.log(e.sum())
+    return out, lse
+
+
+def mha_attention_rows(q, k_nope, k_rope, v, idx, scale: float, kv_len: int):
+    """mha_attention_row over the rows of one sequence: q [R, H, dn + dr],
+    idx [R, k]; returns (out [R, H, dv], lse [R, H])."""
+    outs, lses = zip(*(mha_attention_row(q[r], k_nope, k_rope, v, idx[r], scale, kv_len)
+                       for r in range(len(q))))
+    return np.stack(outs), np.stack(lses)
 
 
 # ---------------------------------------------------------------------------
