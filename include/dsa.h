@@ -85,7 +85,7 @@ typedef struct dsa_problem {
 
 /* Workspace selectors for dsa_workspace_bytes(). */
 enum { DSA_WS_TOPK = 0, DSA_WS_ATTN = 1, DSA_WS_FORWARD = 2, DSA_WS_INDEXER_BWD = 3,
-       DSA_WS_FORWARD_FUSED = 4 };
+       DSA_WS_FORWARD_FUSED = 4, DSA_WS_ATTN_PREFILL = 5 };
 
 /*
  * Stage 1, lightning indexer (r.nikiv.dev summary, "How DSA Works"; the
@@ -161,6 +161,42 @@ dsa_status dsa_topk(const dsa_problem *p, const float *scores, int64_t ld_scores
 dsa_status dsa_sparse_attn(const dsa_problem *p, const uint16_t *q, const uint16_t *kv,
                            const int32_t *topk_idx, uint16_t *out, float *lse,
                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Stage 3 in prefill mode: per-head keys and values.  The threadnavigator.com
+ * thread on DeepSeek-V3.2 (first tweet) notes separate attention modes for
+ * disaggregated prefill and decode; this library reads them as MLA's two
+ * forms of one attention.  dsa_sparse_attn is the decode form (one shared
+ * latent + rope row per key); here every head has its own key -- a 128-wide
+ * part (decompressed from the latent by the caller) followed by the 64-wide
+ * rotary key all heads share -- and its own 128-wide value.  For query row r
+ * of sequence b, with sel(r) the distinct entries of topk_idx[r] in
+ * [0, kv_len_b) and s' = kv_offsets[b] + s:
+ *   logit[h, s] = softmax_scale * (q[r, h, 0:128] . k_nope[s', h, :] +
+ *                                  q[r, h, 128:192] . k_rope[s', :])
+ *   out[r, h, :] = sum_{s in sel(r)} softmax_s(logit[h, :]) * v[s', h, :]
+ *   lse[r, h]    = log(sum_{s in sel(r)} exp(logit[h, s]))     (natural log)
+ * The selection acts as a mask: unlike dsa_sparse_attn, a position listed
+ * twice counts once.  A row with nothing selected gets out = 0, lse = -inf.
+ *   q [total_q, H, 192] bf16           k_nope [total_kv, H, 128] bf16
+ *   k_rope [total_kv, 64] bf16         v [total_kv, H, 128] bf16
+ *   topk_idx [total_q, k] int32        out [total_q, H, 128] bf16
+ *   lse [total_q, H] float (nullable)
+ * Requires heads in 1..128, d_rope = 64 and max_kv_len <= 131072; d_latent
+ * is not used (the per-head widths are fixed).  The work runs over dense
+ * 64-key tiles with the selection applied as a bit mask (tiles that no row of
+ * a 256-row query block selected are skipped), so its cost follows the
+ * selected span rather than k: the form for short prefills, where most of a
+ * row's causal keys are selected.  bf16 MFMA, fp32 softmax and accumulation,
+ * bf16 output rounded to nearest even.
+ * workspace: at least dsa_workspace_bytes(p, DSA_WS_ATTN_PREFILL) bytes,
+ * 16-byte aligned (mostly the row masks, about total_q * max_kv_len / 8
+ * bytes); its contents need no initialisation.
+ */
+dsa_status dsa_sparse_attn_prefill(const dsa_problem *p, const uint16_t *q, const uint16_t *k_nope,
+                                   const uint16_t *k_rope, const uint16_t *v,
+                                   const int32_t *topk_idx, uint16_t *out, float *lse,
+                                   void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * The three stages in order (indexer -> top-k -> attention) on one stream.

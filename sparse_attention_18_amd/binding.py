@@ -23,12 +23,12 @@ DSA_ERR_INVALID_ARGUMENT = 1
 DSA_ERR_UNSUPPORTED = 2
 DSA_ERR_WORKSPACE = 3
 DSA_ERR_HIP = 4
-WS_TOPK, WS_ATTN, WS_FORWARD, WS_INDEXER_BWD, WS_FORWARD_FUSED = 0, 1, 2, 3, 4
+WS_TOPK, WS_ATTN, WS_FORWARD, WS_INDEXER_BWD, WS_FORWARD_FUSED, WS_ATTN_PREFILL = 0, 1, 2, 3, 4, 5
 
 EXPORTED = ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward",
             "dsa_indexer_scores_paged", "dsa_sparse_attn_paged", "dsa_forward_paged",
             "dsa_indexer_align_loss", "dsa_indexer_backward", "dsa_workspace_bytes", "dsa_last_error", "dsa_version",
-            "dsa_forward_noalloc", "dsa_forward_fused")
+            "dsa_forward_noalloc", "dsa_forward_fused", "dsa_sparse_attn_prefill")
 NOALLOC_SCRATCH_BYTES = 256 << 20      # DSA_NOALLOC_SCRATCH_BYTES in include/dsa.h
 
 
@@ -113,10 +113,11 @@ def open_library(path: str):
     lib.dsa_indexer_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, i64, vp, vp, vp, vp, sz, vp]
     lib.dsa_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.dsa_forward_fused.argtypes = [P, G, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.dsa_sparse_attn_prefill.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     for name in ("dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_forward",
                  "dsa_indexer_scores_paged", "dsa_sparse_attn_paged", "dsa_forward_paged",
                  "dsa_indexer_align_loss", "dsa_indexer_backward", "dsa_forward_noalloc",
-                 "dsa_forward_fused"):
+                 "dsa_forward_fused", "dsa_sparse_attn_prefill"):
         getattr(lib, name).restype = ctypes.c_int
     lib.dsa_workspace_bytes.argtypes = [P, ctypes.c_int]
     lib.dsa_workspace_bytes.restype = sz
@@ -263,6 +264,28 @@ def sparse_attn(prob: Problem, q, kv, idx, out, lse=None, workspace=None, stream
         _ptr(idx, torch.int32, "idx", (c.total_q, c.topk)),
         _ptr(out, torch.bfloat16, "out", (c.total_q, c.heads, c.d_latent)),
         _ptr(lse, torch.float32, "lse", (c.total_q, c.heads)), ws_ptr, ws_n, _stream(stream)))
+
+
+MHA_NOPE, MHA_ROPE, MHA_V = 128, 64, 128   # per-head widths of the prefill form
+
+
+def sparse_attn_prefill(prob: Problem, q, k_nope, k_rope, v, idx, out, lse=None, workspace=None,
+                        stream=None):
+    """Stage 3 in prefill mode (dsa_sparse_attn_prefill): per-head keys and values,
+    the selection applied as a mask.  ``workspace`` is a uint8 GPU tensor of at least
+    ``workspace_bytes(prob, WS_ATTN_PREFILL)`` bytes."""
+    c = prob.c
+    if workspace is None:
+        raise ValueError("sparse_attn_prefill needs a workspace tensor")
+    _check(load_library().dsa_sparse_attn_prefill(
+        ctypes.byref(c), _ptr(q, torch.bfloat16, "q", (c.total_q, c.heads, MHA_NOPE + MHA_ROPE)),
+        _ptr(k_nope, torch.bfloat16, "k_nope", (c.total_kv, c.heads, MHA_NOPE)),
+        _ptr(k_rope, torch.bfloat16, "k_rope", (c.total_kv, MHA_ROPE)),
+        _ptr(v, torch.bfloat16, "v", (c.total_kv, c.heads, MHA_V)),
+        _ptr(idx, torch.int32, "idx", (c.total_q, c.topk)),
+        _ptr(out, torch.bfloat16, "out", (c.total_q, c.heads, MHA_V)),
+        _ptr(lse, torch.float32, "lse", (c.total_q, c.heads)),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
 
 
 def forward(prob: Problem, q_fp8, q_scale, w, k_fp8, k_scale, q, kv, out, lse=None,

@@ -377,6 +377,13 @@ size_t dsa_workspace_bytes(const dsa_problem *p, int which) {
       }
       return forward_ws(p, true).total;
     case DSA_WS_INDEXER_BWD: return ws_indexer_bwd(p);
+    case DSA_WS_ATTN_PREFILL:
+      if (p->max_kv_len > dsa::kMhaMaxKvLen) {
+        fail(DSA_ERR_UNSUPPORTED, "dsa_sparse_attn_prefill serves max_kv_len <= %lld",
+             (long long)dsa::kMhaMaxKvLen);
+        return (size_t)-1;
+      }
+      return dsa::mha_workspace_bytes(layout_of(p));
     default: fail(DSA_ERR_INVALID_ARGUMENT, "unknown workspace selector %d", which); return (size_t)-1;
   }
 }
@@ -461,6 +468,51 @@ dsa_status attn_impl(const dsa_problem *p, const dsa_paged_kv *pg, const uint16_
                     "attention launch");
 }
 
+dsa_status prefill_attn_impl(const dsa_problem *p, const uint16_t *q, const uint16_t *k_nope,
+                             const uint16_t *k_rope, const uint16_t *v, const int32_t *topk_idx,
+                             uint16_t *out, float *lse, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+  DSA_TRY(check_problem(p));
+  DSA_CHECK(p->heads >= 1, DSA_ERR_INVALID_ARGUMENT, "heads must be >= 1");
+  DSA_CHECK(p->heads <= 128, DSA_ERR_UNSUPPORTED, "heads must be <= 128 (got %d)", p->heads);
+  DSA_CHECK(p->d_rope == 64, DSA_ERR_UNSUPPORTED,
+            "the prefill form needs d_rope = 64 (per-head keys 128 + 64; got %d)", p->d_rope);
+  DSA_CHECK(p->max_kv_len <= dsa::kMhaMaxKvLen, DSA_ERR_UNSUPPORTED,
+            "the prefill form serves max_kv_len <= %lld (got %lld)", (long long)dsa::kMhaMaxKvLen,
+            (long long)p->max_kv_len);
+  DSA_CHECK(std::isfinite(p->softmax_scale) && p->softmax_scale > 0.f, DSA_ERR_INVALID_ARGUMENT,
+            "softmax_scale must be finite and > 0");
+  const bool hq = p->total_q > 0, hk = p->total_kv > 0;
+  DSA_TRY(check_ptr(q, hq, "q"));
+  DSA_TRY(check_ptr(k_nope, hk, "k_nope"));
+  DSA_TRY(check_ptr(k_rope, hk, "k_rope"));
+  DSA_TRY(check_ptr(v, hk, "v"));
+  DSA_TRY(check_ptr(topk_idx, hq, "topk_idx"));
+  DSA_TRY(check_ptr(out, hq, "out"));
+  if (lse != nullptr) DSA_TRY(check_ptr(lse, hq, "lse"));
+  const size_t need = dsa::mha_workspace_bytes(layout_of(p));
+  DSA_CHECK(workspace_bytes >= need && workspace != nullptr, DSA_ERR_WORKSPACE,
+            "prefill attention workspace needs %zu bytes (got %zu)", need, workspace_bytes);
+  DSA_CHECK(aligned16(workspace), DSA_ERR_INVALID_ARGUMENT, "workspace must be 16-byte aligned");
+  DSA_DEBUG_CHECK(p, nullptr, stream);
+  dsa::MhaArgs a;
+  a.seq = layout_of(p);
+  a.q = q;
+  a.k_nope = k_nope;
+  a.k_rope = k_rope;
+  a.v = v;
+  a.idx = topk_idx;
+  a.out = out;
+  a.lse = lse;
+  a.heads = p->heads;
+  a.k = p->topk;
+  a.scale = p->softmax_scale;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
+  return hip_status(dsa::launch_mha_prefill(a, static_cast<hipStream_t>(stream)),
+                    "prefill attention launch");
+}
+
 dsa_status forward_impl(const dsa_problem *p, const dsa_paged_kv *pg, const uint8_t *q_fp8,
                         const float *q_scale, const float *w, const uint8_t *k_fp8,
                         const float *k_scale, const uint16_t *q, const uint16_t *kv, uint16_t *out,
@@ -508,6 +560,14 @@ dsa_status dsa_sparse_attn(const dsa_problem *p, const uint16_t *q, const uint16
                            const int32_t *topk_idx, uint16_t *out, float *lse, void *workspace,
                            size_t workspace_bytes, void *stream) {
   return attn_impl(p, nullptr, q, kv, topk_idx, out, lse, workspace, workspace_bytes, stream);
+}
+
+dsa_status dsa_sparse_attn_prefill(const dsa_problem *p, const uint16_t *q, const uint16_t *k_nope,
+                                   const uint16_t *k_rope, const uint16_t *v,
+                                   const int32_t *topk_idx, uint16_t *out, float *lse,
+                                   void *workspace, size_t workspace_bytes, void *stream) {
+  return prefill_attn_impl(p, q, k_nope, k_rope, v, topk_idx, out, lse, workspace, workspace_bytes,
+                           stream);
 }
 
 dsa_status dsa_sparse_attn_paged(const dsa_problem *p, const dsa_paged_kv *pg, const uint16_t *q,

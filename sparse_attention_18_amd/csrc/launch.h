@@ -83,6 +83,25 @@ struct AttnArgs {
   int32_t nsplit;    // workgroups per token (set by the launcher)
 };
 
+// Prefill-mode attention: per-head keys (a 128-wide part and a 64-wide
+// rotary part shared by the heads) and per-head 128-wide values, the
+// selected positions applied as a mask over dense key tiles.
+struct MhaArgs {
+  SeqLayout seq;
+  const uint16_t *q;        // [total_q, heads, 192]
+  const uint16_t *k_nope;   // [total_kv, heads, 128]
+  const uint16_t *k_rope;   // [total_kv, 64]
+  const uint16_t *v;        // [total_kv, heads, 128]
+  const int32_t *idx;       // [total_q, k]
+  uint16_t *out;            // [total_q, heads, 128]
+  float *lse;               // [total_q, heads] or nullptr
+  int32_t heads, k;
+  float scale;
+  void *workspace;
+  size_t workspace_bytes;
+};
+constexpr int64_t kMhaMaxKvLen = 131072;   // a row's mask is built in LDS
+
 // Indexer alignment loss: idx == nullptr selects the dense warm-up form (all
 // causal keys); grad rows are ld_grad apart (dense: by key position; sparse:
 // by entry of idx).
@@ -134,6 +153,8 @@ hipError_t launch_indexer_backward(const IndexerBwdArgs &a, hipStream_t stream);
 hipError_t launch_align_loss(const AlignArgs &a, hipStream_t stream);
 hipError_t launch_topk(const TopkArgs &a, hipStream_t stream);
 hipError_t launch_sparse_attn(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_mha_prefill(const MhaArgs &a, hipStream_t stream);
+size_t mha_workspace_bytes(const SeqLayout &seq);
 // Top-k from the fused data of a decode indexer launch (a.fuse set, a.scores
 // the same launch's scores for the exact fallback).
 hipError_t launch_topk_fused(const TopkArgs &a, hipStream_t stream);

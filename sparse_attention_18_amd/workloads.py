@@ -238,3 +238,20 @@ def paged_caches(inp: dict, block_size: int, seed: int = 0, extra_blocks: int = 
     kv_cache[dst] = kv[src]
     return (table, num_blocks, k_cache.view(num_blocks, block_size, -1),
             ks_cache.view(num_blocks, block_size), kv_cache.view(num_blocks, block_size, -1))
+
+
+# Prefill-mode (per-head) attention: per-head widths of that form.
+MHA_NOPE, MHA_ROPE, MHA_V = 128, 64, 128
+
+
+def mha_prefill_inputs(q_rows: int, kv_rows: int, heads: int, seed: int, device="cpu",
+                       std: float = 1.0) -> dict:
+    """Seeded inputs of the prefill-mode attention: q [q_rows, heads, 192],
+    k_nope [kv_rows, heads, 128], k_rope [kv_rows, 64], v [kv_rows, heads, 128],
+    each N(0, std^2) in bfloat16 (the law of keys and values decompressed from
+    unit-variance latents by projections of unit gain)."""
+    gen = torch.Generator(device=device).manual_seed(seed)
+    return dict(q=_randn_bf16((q_rows, heads, MHA_NOPE + MHA_ROPE), std, gen, device),
+                k_nope=_randn_bf16((kv_rows, heads, MHA_NOPE), std, gen, device),
+                k_rope=_randn_bf16((kv_rows, MHA_ROPE), std, gen, device),
+                v=_randn_bf16((kv_rows, heads, MHA_V), std, gen, device))

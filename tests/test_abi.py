@@ -329,3 +329,33 @@ def test_indexer_backward_two_pass_workspace():
     assert "indexer backward workspace" in _msg()
     assert _ibwd(p, ws=FAKE + 4, ws_n=need) == binding.DSA_ERR_INVALID_ARGUMENT
     assert "aligned" in _msg()
+
+
+def _prefill(p, q=FAKE, out=FAKE, ws=FAKE, ws_n=1 << 40):
+    lib = binding.load_library()
+    return lib.dsa_sparse_attn_prefill(ctypes.byref(p) if p is not None else None, q, FAKE, FAKE, FAKE,
+                                       FAKE, out, None, ws, ws_n, None)
+
+
+def test_prefill_attention_checks_its_shape_and_workspace():
+    """dsa_sparse_attn_prefill: per-head widths fixed (d_rope must be 64),
+    heads 1..128, rows of at most 131072 keys, a workspace of about
+    total_q * max_kv_len / 8 bytes (the row masks); each refused before a
+    launch."""
+    lib = binding.load_library()
+    p = _problem()                                     # 4096-row prefill, 128 heads
+    need = lib.dsa_workspace_bytes(ctypes.byref(p), binding.WS_ATTN_PREFILL)
+    masks = (4096 // 256 + 1) * (4096 // 64) * 256 * 8
+    assert masks <= need < masks + (1 << 20)
+    assert _prefill(_problem(d_rope=32)) == binding.DSA_ERR_UNSUPPORTED and "d_rope" in _msg()
+    assert _prefill(_problem(heads=129)) == binding.DSA_ERR_UNSUPPORTED and "heads" in _msg()
+    assert _prefill(_problem(heads=0)) == binding.DSA_ERR_INVALID_ARGUMENT
+    big = _problem(total_kv=131073, max_kv_len=131073)
+    assert _prefill(big) == binding.DSA_ERR_UNSUPPORTED and "131072" in _msg()
+    assert lib.dsa_workspace_bytes(ctypes.byref(big), binding.WS_ATTN_PREFILL) == ctypes.c_size_t(-1).value
+    assert _prefill(p, ws_n=need - 1) == binding.DSA_ERR_WORKSPACE
+    assert _prefill(p, ws=None) == binding.DSA_ERR_WORKSPACE
+    assert _prefill(p, ws=FAKE + 8) == binding.DSA_ERR_INVALID_ARGUMENT
+    assert _prefill(p, q=None) == binding.DSA_ERR_INVALID_ARGUMENT and "q is NULL" in _msg()
+    assert _prefill(p, out=FAKE + 4) == binding.DSA_ERR_INVALID_ARGUMENT
+    assert _prefill(None) == binding.DSA_ERR_INVALID_ARGUMENT
