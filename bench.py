@@ -200,7 +200,8 @@ def measured_peaks(dev):
     return res
 
 
-_SPEC = {"hbm": (HBM_PEAK, "GB/s", 1e9), "mfma": (FP8_PEAK, "TFLOP/s", 1e12)}
+_SPEC = {"hbm": (HBM_PEAK, "GB/s", 1e9), "mfma": (FP8_PEAK, "TFLOP/s", 1e12),
+         "mfma_bf16": (BF16_PEAK, "TFLOP/s", 1e12)}
 
 
 def _measured_peak(bound, peaks):
@@ -208,7 +209,7 @@ def _measured_peak(bound, peaks):
         return None
     if bound == "hbm":
         return max(peaks["hbm_copy_GBps"], peaks["hbm_read_GBps"]) * 1e9
-    v = peaks.get("fp8_gemm_TFLOPs")
+    v = peaks.get("bf16_gemm_TFLOPs" if bound == "mfma_bf16" else "fp8_gemm_TFLOPs")
     return v * 1e12 if v else None
 
 
@@ -416,7 +417,39 @@ def run_prefill_single(wl, dev, flush, peaks=None, iters=10, warmup=2):
     res = {"workload": wl.name, "tokens_per_s": round(L / (total * 1e-3), 1), "ms": round(total, 4),
            "iters": iters, "mall_flushed": True, "stages": stages}
     del scores, out, lse, tws, aws
+    res["prefill_mode_attention"] = run_prefill_mode(wl, dev, flush, prob, idx, med[2], peaks, iters, warmup)
     return res, inp, idx
+
+
+def run_prefill_mode(wl, dev, flush, prob, idx, absorbed_ms, peaks, iters, warmup):
+    """The same selection through the prefill-mode attention (per-head keys of
+    128 + 64 and values of 128, the selection as a mask over dense key tiles),
+    on seeded inputs of that form.  Its roofline is bf16 MFMA on the dense work
+    it does (every causal pair of the tiles it visits, here all of them); the
+    flops of the selected pairs alone are reported beside it."""
+    L, H = wl.seq_len, wl.heads
+    inp = wk.mha_prefill_inputs(L, L, H, seed=wl.seed + 100, device=dev)
+    out = torch.empty(L, H, wk.MHA_V, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(L, H, dtype=torch.float32, device=dev)
+    ws = torch.empty(dsa.workspace_bytes(prob, dsa.WS_ATTN_PREFILL), dtype=torch.uint8, device=dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(warmup + iters)]
+    for i in range(warmup + iters):
+        flush()
+        evs[i][0].record()
+        dsa.sparse_attn_prefill(prob, inp["q"], inp["k_nope"], inp["k_rope"], inp["v"], idx, out, lse, ws)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.median([e[0].elapsed_time(e[1]) for e in evs[warmup:]]))
+    per_pair = 2 * H * (wk.MHA_NOPE + wk.MHA_ROPE + wk.MHA_V)
+    causal = L * (L + 1) // 2
+    selected = int((idx >= 0).sum())
+    e = stage_entry(ms, 1, "mfma_bf16", per_pair * causal, peaks)
+    e["selected_pair_tflops"] = round(per_pair * selected / (ms * 1e-3) / 1e12, 1)
+    e["vs_absorbed_form"] = round(absorbed_ms / ms, 3)
+    log(f"[bench] {wl.name}: prefill-mode attention {ms:.3f} ms ({e['achieved']} TFLOP/s on the causal "
+        f"pairs, {e['frac']:.3f} of bf16 peak; absorbed form {absorbed_ms:.3f} ms)")
+    del inp, out, lse, ws
+    return e
 
 
 def run_train(bench, steps=2):
