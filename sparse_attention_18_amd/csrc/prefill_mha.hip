@@ -36,7 +36,8 @@
 //      softmax in a lazily moved exponent frame, then O^T += V^T . P^T
 //      (P straight from the S^T registers, V^T through transposing LDS
 //      reads).  Tiles (K nope, K rope, V, mask words) arrive by LDS-DMA in a
-//      three-stage ring, two tiles ahead of the compute.
+//      three-stage ring, one tile ahead of the compute; the two waves of a
+//      SIMD run their phases in opposite order.
 #include "common.h"
 #include "kv_gather.h"
 #include "launch.h"
@@ -219,7 +220,7 @@ __global__ __launch_bounds__(512) void mha_tiles_kernel(MhaWs w) {
 // ---- 4. attention -------------------------------------------------------
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void mha_prefill_kernel(MhaArgs p, MhaWs w) {
-  __shared__ __attribute__((aligned(1024))) uint8_t tiles[kMStages][kMStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t tiles[kMStages * kMStageBytes];
 
   const int tid = __builtin_amdgcn_workitem_id_x(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -262,7 +263,7 @@ void mha_prefill_kernel(MhaArgs p, MhaWs w) {
   // Row-data block: slot i holds row 16 rb + i / 4, chunk 4 cq + ((i % 4) ^ (i / 16)).
   const int ri = lane >> 2, lc = (lane & 3) ^ (lane >> 4);
   const int64_t kv0 = s.kv0;
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(DSA_LDS uint8_t *)tiles[0];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(DSA_LDS uint8_t *)tiles;
   auto issue = [&](int tile, int stage) {
     // listed tiles start inside the sequence: 1 <= rows_valid <= 64
     const int rows_valid = (int)(s.kvlen - (int64_t)tile * kMKB < kMKB ? s.kvlen - (int64_t)tile * kMKB : kMKB);
@@ -298,7 +299,6 @@ void mha_prefill_kernel(MhaArgs p, MhaWs w) {
       }
     }
   };
-  const bool extra = wave < kBStage - 5 * kMWaves;   // waves with a sixth block
 
   // ---- per-lane LDS offsets
   // S^T A operand, key half kh, k-step ks: row 32 kh + j, chunk 2 ks' + G
@@ -337,20 +337,8 @@ void mha_prefill_kernel(MhaArgs p, MhaWs w) {
   float m_used = -1e30f;                         // exponent frame (log2 units); no key yet
   const float c2 = p.scale * kLog2e;
 
-  if (ntiles > 0) issue(tl[0], 0);
-  if (ntiles > 1) issue(tl[1], 1);
-  for (int t = 0; t < ntiles; ++t) {
-    // this wave's blocks of tile t have landed (those of t + 1 may still fly)
-    if (t + 1 < ntiles) {
-      if (extra) wait_vmcnt<6>();
-      else wait_vmcnt<5>();
-    } else {
-      wait_vmcnt<0>();
-    }
-    __syncthreads();              // tile t visible; every wave is done with tile t - 1's stage
-    if (t + 2 < ntiles) issue(tl[t + 2], (t + 2) % kMStages);
-    const DSA_LDS uint8_t *tb = (const DSA_LDS uint8_t *)tiles[t % kMStages];
-
+  // Phase 1 of a tile: S^T, mask, frame, P (bf16, registers).
+  auto qk_softmax = [&](const DSA_LDS uint8_t *tb, v8bf (&pk)[2][2]) {
     // S^T: two 32-key halves, 12 dependent k-steps each, interleaved
     // (step i: half i % 2, k-step i / 2); A operands read kLA steps ahead.
     constexpr int kSteps = 2 * (kMQ / 16), kLA = 4;
@@ -390,7 +378,6 @@ void mha_prefill_kernel(MhaArgs p, MhaWs w) {
       m_used = mt;
     }
     // P = 2^(logit * c2 - frame); masked logits give 0
-    v8bf pk[2][2];
     float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh)
@@ -402,10 +389,11 @@ void mha_prefill_kernel(MhaArgs p, MhaWs w) {
         pk[kh][r >> 3][r & 7] = (__bf16)pe;
       }
     l_part += ls0 + ls1;
-
-    // O^T[dims][rows] += V^T . P^T: 16 independent MFMAs (step i: k-step
-    // (kh, hf) = (i / 8, (i / 4) % 2), dims block u = i % 4), V^T read two
-    // steps ahead.
+  };
+  // Phase 2: O^T[dims][rows] += V^T . P^T, 16 independent MFMAs (step i:
+  // k-step (kh, hf) = (i / 8, (i / 4) % 2), dims block u = i % 4), V^T read
+  // two steps ahead.
+  auto pv = [&](const DSA_LDS uint8_t *tb, const v8bf (&pk)[2][2]) {
     constexpr int kPV = 16, kVA = 2;
     v8bf va[kVA];
 #pragma unroll
@@ -416,7 +404,36 @@ void mha_prefill_kernel(MhaArgs p, MhaWs w) {
       if (i + kVA < kPV) va[i % kVA] = load_vt(tb, (i + kVA) >> 3, ((i + kVA) >> 2) & 1, (i + kVA) & 3);
       __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  // The two waves of a SIMD (w and w + 4) run the phases in opposite order:
+  // waves 0-3 do S^T, softmax, P.V of tile t; waves 4-7 start step t with
+  // the P.V of tile t - 1 (its P kept in registers, its frame still the
+  // one P was made in) and keep tile t's P for the next step.  One wave's
+  // softmax then runs while the other issues MFMAs.  Tile t + 1 is loaded
+  // during step t into stage (t + 1) % 3, which step t - 1's P.V (deferred
+  // or not) no longer reads once the step's barrier has passed.
+  const bool defer = wave >= kMWaves / 2;
+  v8bf pk[2][2];                  // P of the tile whose P.V is pending
+  if (ntiles > 0) issue(tl[0], 0);
+  // stage bases as scalars (LDS byte addresses), so that every operand read
+  // is one scalar base + the lane's offset + an immediate
+  auto stage_ptr = [&](int st) {
+    return (const DSA_LDS uint8_t *)tiles + __builtin_amdgcn_readfirstlane(st * kMStageBytes);
+  };
+  int st_cur = 0, st_prev = kMStages - 1;
+  for (int t = 0; t < ntiles; ++t) {
+    wait_vmcnt<0>();              // this wave's blocks of tile t have landed
+    __syncthreads();              // tile t visible; stage (t + 1) % 3 free
+    const int st_next = st_cur == kMStages - 1 ? 0 : st_cur + 1;
+    if (t + 1 < ntiles) issue(tl[t + 1], st_next);
+    if (defer && t > 0) pv(stage_ptr(st_prev), pk);
+    qk_softmax(stage_ptr(st_cur), pk);
+    if (!defer) pv(stage_ptr(st_cur), pk);
+    st_prev = st_cur;
+    st_cur = st_next;
   }
+  if (defer && ntiles > 0) pv(stage_ptr(st_prev), pk);
 
   // ---- epilogue: lane (G, j) holds row j's dims 32 u + 8 (e / 4) + 4 G + e % 4
   const float l_tot = sum_across_halves(l_part);

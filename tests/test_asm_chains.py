@@ -70,10 +70,12 @@ def chain_hazards(body):
 
 
 def _kernels(asm):
+    """(name, lines) of each attention kernel, up to its end-of-function label
+    (blocks after an early s_endpgm belong to it too)."""
     lines = asm.split("\n")
     starts = [i for i, l in enumerate(lines) if re.match(r"^_Z\S*mla_sparse_attn_kernel\S*:", l)]
     for st in starts:
-        en = next(i for i in range(st, len(lines)) if "s_endpgm" in lines[i])
+        en = next(i for i in range(st, len(lines)) if lines[i].startswith(".Lfunc_end"))
         yield lines[st].split(":")[0], lines[st:en]
 
 
