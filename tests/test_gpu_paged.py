@@ -2,7 +2,9 @@
 KV caches gives the same result from block-table caches as from the packed
 ones (bit-identical: the same arithmetic in the same order), and the oracle's
 on the logical rows.  Block tables are shuffled, leave unused blocks, and in
-one case place the used blocks past 4 GB of the latent cache."""
+one case place the used blocks past 4 GB of the latent cache.  The decode
+workload at full size (64 sequences, 8K-128K contexts) also runs through the
+paged forward and is checked against the oracle directly."""
 import math
 
 import numpy as np
@@ -130,3 +132,35 @@ def test_paged_forward_decode_matches_packed():
         outs.append((out, lse, idx))
     for a, b in zip(outs[0], outs[1]):
         assert torch.equal(a, b)
+
+
+def test_paged_forward_decode_full_size_against_the_oracle():
+    """The decode workload at full size (64 sequences, contexts 8K-128K)
+    through dsa_forward_paged over shuffled 64-row blocks, checked against the
+    oracle directly: indexer scores of 8 sequences, every row's selection
+    (bit-exact against the oracle selector on the GPU's own scores) and every
+    row's attention."""
+    wl = wk.DECODE_B64
+    _announce("forward decode B=64 ctx 8K..128K, paged (block 64), against the oracle")
+    inp = wk.generate(wl, device="cuda")
+    prob = dsa.Problem.from_workload(wl, inp, device="cuda")
+    B = wl.decode_batch
+    ws = torch.empty(dsa.workspace_bytes(prob, dsa.WS_FORWARD), dtype=torch.uint8, device="cuda")
+    out = torch.empty(B, wl.heads, wl.d_latent, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, wl.heads, dtype=torch.float32, device="cuda")
+    idx = torch.empty(B, wl.topk, dtype=torch.int32, device="cuda")
+    pg, kc, ksc, kvc = H.make_paged(inp, 64, seed=21)
+    dsa.forward_paged(prob, pg, inp["q_fp8"], inp["q_scale"], inp["w"], kc, ksc, inp["q"], kvc, out, lse,
+                      idx, ws)
+    torch.cuda.synchronize()
+    del kc, ksc, kvc
+    ld = prob.ld_scores()
+    scores = ws[: B * ld * 4].view(torch.float32).view(B, ld)      # dsa_forward keeps them first
+    offs = [int(x) for x in inp["kv_offsets"]]
+    pos = [int(x) for x in inp["q_pos0"]]
+    for b in (0, 1, 17, 31, 40, 50, 62, 63):
+        refs = H.oracle_scores_for_rows(inp, slice(b, b + 1), offs[b], [pos[b]])
+        H.check_indexer_rows(scores, refs, [b])
+    rows = list(range(B))
+    H.check_topk_rows(idx, scores, rows, [p + 1 for p in pos], wl.topk)
+    H.check_attention_rows(out, lse, inp["q"], inp["kv"], idx, rows, offs[:-1], wl.softmax_scale, wl.d_latent)
