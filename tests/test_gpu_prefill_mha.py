@@ -161,3 +161,27 @@ def test_prefill_mha_4k_full_size():
     assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
     rows = [0, 1, 255, 256, 1023, 2046, 2047, 2048, 2049, 3071, 3584, 4095]
     _check(inp, out, lse, idx_cpu, rows, [0, L], [0, L], [0])
+
+
+def test_prefill_mha_null_lse_and_no_rows():
+    """lse is optional (same out bit for bit without it); a problem with no
+    query rows returns without launching anything."""
+    _announce("prefill-mode attention, lse NULL and an empty problem")
+    q_lens, kv_lens, p0 = [150], [150], [0]
+    idx = _selection(q_lens, kv_lens, p0, 32, seed=8)
+    inp, out, lse, qo, ko = _run(q_lens, kv_lens, p0, 4, 32, idx, seed=9)
+    prob = dsa.Problem(q_offsets=qo, kv_offsets=ko, q_pos0=p0, idx_heads=64, idx_dim=128, heads=4,
+                       d_latent=512, d_rope=64, topk=32, softmax_scale=SCALE, device=DEV)
+    out2 = torch.full_like(out, float("nan"))
+    ws = torch.empty(dsa.workspace_bytes(prob, dsa.WS_ATTN_PREFILL), dtype=torch.uint8, device=DEV)
+    dsa.sparse_attn_prefill(prob, inp["q"], inp["k_nope"], inp["k_rope"], inp["v"], idx.to(DEV), out2, None, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    empty = dsa.Problem(q_offsets=[0, 0], kv_offsets=[0, 150], q_pos0=[0], idx_heads=64, idx_dim=128, heads=4,
+                        d_latent=512, d_rope=64, topk=32, softmax_scale=SCALE, device=DEV)
+    z = torch.empty(0, 4, 192, dtype=torch.bfloat16, device=DEV)
+    zo = torch.empty(0, 4, 128, dtype=torch.bfloat16, device=DEV)
+    zi = torch.empty(0, 32, dtype=torch.int32, device=DEV)
+    ws0 = torch.empty(dsa.workspace_bytes(empty, dsa.WS_ATTN_PREFILL), dtype=torch.uint8, device=DEV)
+    dsa.sparse_attn_prefill(empty, z, inp["k_nope"], inp["k_rope"], inp["v"], zi, zo, None, ws0)
+    torch.cuda.synchronize()
