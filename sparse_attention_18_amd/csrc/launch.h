@@ -229,6 +229,38 @@ __device__ __forceinline__ int find_seq(const SeqLayout &L, int64_t r) {
   return cnt > 0 ? cnt - 1 : 0;
 }
 
+// find_seq in two halves, so that the offset loads can go out early and
+// other loads behind them: find_seq_issue loads this lane's four candidate
+// offsets among the first 256 sequences (addresses clamped, so the loads are
+// unconditional); find_seq_done counts them like find_seq (searching on for
+// batches beyond 256).  Same requirements as find_seq.
+__device__ __forceinline__ void find_seq_issue(const SeqLayout &L, int (&o)[4]) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = 64 * u + lane;
+    o[u] = L.q_offsets[i < L.batch ? i : L.batch - 1];
+  }
+}
+
+__device__ __forceinline__ int find_seq_done(const SeqLayout &L, int64_t r, const int (&o)[4]) {
+  const int lane = __lane_id();
+  int cnt = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) cnt += __popcll(__ballot(64 * u + lane < L.batch && (int64_t)o[u] <= r));
+  for (int base = 256; base < L.batch; base += 256) {
+    bool le[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = base + 64 * u + lane;
+      le[u] = i < L.batch && (int64_t)L.q_offsets[i] <= r;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) cnt += __popcll(__ballot(le[u]));
+  }
+  return cnt > 0 ? cnt - 1 : 0;
+}
+
 // Cache row of key position pos (0 <= pos < s.kvlen) of sequence b.  With a
 // block table, the block index and the table entry are clamped in bounds.
 template <bool kPaged>
@@ -259,6 +291,20 @@ __device__ __forceinline__ int row_seq(const SeqLayout &L, int64_t r, SeqInfo &s
     return rr;
   }
   const int b = find_seq(L, r);
+  s = load_seq(L, b);
+  return b;
+}
+
+// row_seq with the search offsets already loaded by find_seq_issue.
+__device__ __forceinline__ int row_seq_issued(const SeqLayout &L, int64_t r, const int (&o)[4], SeqInfo &s) {
+  const int rr = (int)(r < L.batch ? r : L.batch - 1);
+  const int64_t q0 = L.q_offsets[rr], q1 = L.q_offsets[rr + 1];
+  const int64_t k0 = L.kv_offsets[rr], k1 = L.kv_offsets[rr + 1], p0 = L.q_pos0[rr];
+  if (r < L.batch && q0 == r && q1 == r + 1) {
+    s = clamp_seq(L, q0, q1, k0, k1, p0);
+    return rr;
+  }
+  const int b = find_seq_done(L, r, o);
   s = load_seq(L, b);
   return b;
 }

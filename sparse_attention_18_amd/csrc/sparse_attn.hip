@@ -110,10 +110,25 @@ void mla_sparse_attn_kernel(AttnArgs p) {
   const int G = lane >> 5, c32 = lane & 31, jl = lane & 15, half = (lane >> 4) & 1;
   const int k = p.k;
 
+  // Loads go out in this order: the row's index entries, the sequence
+  // search's offsets, then the Q^T operands.  The vector memory counter
+  // completes in issue order, so the wait for the first two groups leaves the
+  // Q^T loads in flight through the sequence lookup, the compaction and the
+  // first tile's gather.  All of them are unconditional (clamped addresses),
+  // so the compiler counts them exactly.
+  constexpr int per = kMaxK / T;             // entries per thread (k <= kMaxK)
+  int raw[per];
+  {
+    const int32_t *idx_row = p.idx + t * k;  // row t < total_q: in bounds
+    const int i0 = tid * per;
+#pragma unroll
+    for (int e = 0; e < per; ++e) raw[e] = idx_row[i0 + e < k ? i0 + e : k - 1];
+  }
+  int soff[4];
+  find_seq_issue(p.seq, soff);
+  __builtin_amdgcn_sched_barrier(0);
   // Q^T operands of this wave's heads: k-step kk = dims 16kk..16kk+15, lane
-  // (G, c32) holds head 32*wave + c32, dims 16kk + 8G .. +7.  Row t < total_q
-  // is always in bounds.  Issued first: they depend on t only, so their
-  // latency overlaps the sequence lookup and the index compaction.
+  // (G, c32) holds head 32*wave + c32, dims 16kk + 8G .. +7.
   const int head = wave * 32 + c32;
   v8bf qb[kD / 16];
   {
@@ -122,24 +137,21 @@ void mla_sparse_attn_kernel(AttnArgs p) {
     for (int kk = 0; kk < kD / 16; ++kk)
       qb[kk] = as_v8bf(*reinterpret_cast<const v4i *>(qrow + 16 * kk));
   }
+  __builtin_amdgcn_sched_barrier(0);
 
   SeqInfo s;
-  const int b = row_seq(p.seq, t, s);
+  const int b = row_seq_issued(p.seq, t, soff, s);
   const bool row_ok = t >= s.q0 && t < s.q1;
 
   // Compact the row's valid indices (in order) into idxl; m = their count.
   int m;
   {
-    constexpr int per = kMaxK / T;           // entries per thread (k <= kMaxK)
-    const int32_t *idx_row = p.idx + t * k;
     const int i0 = tid * per;
     int vals[per];
     int cnt = 0;
 #pragma unroll
     for (int e = 0; e < per; ++e) {
-      const int i = i0 + e;
-      int v = -1;
-      if (row_ok && i < k) v = idx_row[i];
+      const int v = (row_ok && i0 + e < k) ? raw[e] : -1;
       vals[e] = (v >= 0 && v < s.kvlen) ? v : -1;
       cnt += vals[e] >= 0;
     }
@@ -173,7 +185,6 @@ void mla_sparse_attn_kernel(AttnArgs p) {
   const int nrows = r_end - r_begin;
   const int ntiles = (nrows + kBN - 1) / kBN;
   const int *idxr = idxl + r_begin;
-  wait_vmcnt<0>();   // Q^T operands resident before any LDS-DMA is in flight
 
   // Gather of tile `tl` into its stage buffer; rows past m repeat a valid
   // row.  This wave owns row blocks rb = wave + NW*q (q < kRB); the load of
