@@ -59,6 +59,11 @@ def test_paged_indexer_prefill_matches_packed(bs, r0, r1):
     dsa.indexer_scores_paged(prob, pg, g["q_fp8"], g["q_scale"], g["w"], kc, ksc, sc, prob.ld_scores())
     torch.cuda.synchronize()
     assert torch.equal(torch.nan_to_num(sc, nan=-7.0), torch.nan_to_num(ref, nan=-7.0))
+    # and the oracle on the logical rows: the first, the last and a spread between
+    local = sorted({0, 1, (r1 - r0) // 3, (r1 - r0) // 2, r1 - r0 - 2, r1 - r0 - 1})
+    for i in local:
+        refs = H.oracle_scores_for_rows(sub, slice(i, i + 1), 0, [r0 + i])
+        H.check_indexer_rows(sc, refs, [i])
 
 
 def _attn_inputs(T, S, k, H_, dl, dr, seed, fill=None):
