@@ -156,7 +156,7 @@ dsa_status dsa_topk(const dsa_problem *p, const float *scores, int64_t ld_scores
  * workspace: at least dsa_workspace_bytes(p, DSA_WS_ATTN) bytes.  It is zero
  * for large batches; batches of fewer than 128 tokens split each token's
  * selected rows over several workgroups and need room for the partial
- * results (nsplit * total_q * H * 2056 bytes).
+ * results (nsplit * total_q * H * 1048 bytes).
  */
 dsa_status dsa_sparse_attn(const dsa_problem *p, const uint16_t *q, const uint16_t *kv,
                            const int32_t *topk_idx, uint16_t *out, float *lse,

@@ -38,8 +38,9 @@
 //
 // Few tokens (decode): the token's compacted index list is cut into nsplit
 // contiguous ranges, one workgroup each, so that the batch fills the chip.
-// Each range's workgroup writes its unnormalised O, its exponent frame and its
-// softmax denominator per head to the workspace; a small combine kernel then
+// Each range's workgroup writes its unnormalised O (fp16 with a power-of-two
+// scale per head and wave), its exponent frame and its softmax denominator
+// per head to the workspace; a small combine kernel then
 // rescales the ranges to their common maximum frame (the usual merge of
 // partial softmax sums) and writes out and lse.
 #include <type_traits>
@@ -55,6 +56,13 @@ constexpr int kStages = 3;
 constexpr int kMaxK = 4096;
 constexpr float kFrameSlack = 32.f;          // log2 headroom above the frame max
 constexpr int kMaxSplits = 4;                // workgroups per token in the split path
+constexpr int kMaxWaves = 4;                 // scales per (split, token, head) in the split path
+
+// Two floats to fp16 bits (round to nearest even), packed low | high.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
 
 // S^T accumulation MFMAs, pinned to VGPRs.  The P.V accumulators fill all
 // 256 AGPRs; left to itself the compiler puts this accumulator in AGPRs too
@@ -409,22 +417,40 @@ void mla_sparse_attn_kernel(AttnArgs p) {
 
   const float l_tot = sum_across_halves(l_part);
   if (p.nsplit > 1) {
-    // ---- partial epilogue: unnormalised O^T, frame and denominator per head
+    // ---- partial epilogue: the frame and denominator per head, and the
+    // unnormalised O^T in fp16 (round to nearest) after a power-of-two scale
+    // per (head, wave) that brings the wave's DW dims of the head into
+    // [-1, 1]: 2^-11 relative per element, and no overflow for any finite O.
     if (!row_ok) return;
     const int64_t slot = (int64_t)split * p.seq.total_q + t;
-    float *wo = reinterpret_cast<float *>(p.workspace) + slot * H * (int64_t)kDL;
-    float2 *wml = reinterpret_cast<float2 *>(reinterpret_cast<float *>(p.workspace) +
-                                             (int64_t)p.nsplit * p.seq.total_q * H * kDL);
+    const int64_t nslot = (int64_t)p.nsplit * p.seq.total_q;
+    uint16_t *wo = reinterpret_cast<uint16_t *>(p.workspace) + slot * H * (int64_t)kDL;
+    float2 *wml = reinterpret_cast<float2 *>(reinterpret_cast<uint16_t *>(p.workspace) + nslot * H * kDL);
+    float *wsc = reinterpret_cast<float *>(wml + nslot * H);
     if (G == 0) wml[slot * H + head] = make_float2(m_used, l_tot);
 #pragma unroll
     for (int nb = 0; nb < NW; ++nb) {
-      float *ohead = wo + (nb * 32 + c32) * (int64_t)kDL + wave * DW + 4 * G;
+      float mx = 0.f;
 #pragma unroll
       for (int u = 0; u < MB; ++u)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<v4f *>(ohead + 32 * u + 8 * i) =
-              v4f{o[u][nb][4 * i], o[u][nb][4 * i + 1], o[u][nb][4 * i + 2], o[u][nb][4 * i + 3]};
+        for (int j = 0; j < 16; ++j) mx = fmaxf(mx, fabsf(o[u][nb][j]));
+      mx = max_across_halves(mx);   // the head's other half of the wave's dims
+      // mx = f 2^e with f in [0.5, 1); e is clamped so both 2^e and 2^-e are
+      // normal floats (a head whose values are all below 2^-100 keeps zeros)
+      int e = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) : 0;
+      e = e < -100 ? -100 : e;
+      const float inv = ldexpf(1.f, -e);
+      if (G == 0) wsc[(slot * H + nb * 32 + c32) * kMaxWaves + wave] = ldexpf(1.f, e);
+      uint16_t *ohead = wo + (nb * 32 + c32) * (int64_t)kDL + wave * DW + 4 * G;
+#pragma unroll
+      for (int u = 0; u < MB; ++u)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t w0 = pack_f16x2(o[u][nb][4 * i] * inv, o[u][nb][4 * i + 1] * inv);
+          const uint32_t w1 = pack_f16x2(o[u][nb][4 * i + 2] * inv, o[u][nb][4 * i + 3] * inv);
+          *reinterpret_cast<v2i *>(ohead + 32 * u + 8 * i) = v2i{(int)w0, (int)w1};
+        }
     }
     return;
   }
@@ -466,17 +492,21 @@ __global__ __launch_bounds__(128) void combine_splits_kernel(AttnArgs p, int hea
   if (t < s.q0 || t >= s.q1) return;
   const int S = p.nsplit;   // 2..kMaxSplits
   const int64_t per_split = p.seq.total_q * heads;
-  const float *wo = reinterpret_cast<const float *>(p.workspace);
+  const uint16_t *wo = reinterpret_cast<const uint16_t *>(p.workspace);
   const float2 *wml = reinterpret_cast<const float2 *>(wo + (int64_t)S * per_split * kDL);
+  const float *wsc = reinterpret_cast<const float *>(wml + (int64_t)S * per_split);
+  const int wv = 4 * tid / (kDL / (heads / 32));   // the wave that held these dims
   // Every split's loads are issued before any is used (clamped to the last
   // split past S, whose weight is then zero).
   float2 ml[kMaxSplits];
-  v4f x[kMaxSplits];
+  float sc[kMaxSplits];
+  v2i x[kMaxSplits];
 #pragma unroll
   for (int sp = 0; sp < kMaxSplits; ++sp) {
     const int64_t at = (int64_t)(sp < S ? sp : S - 1) * per_split + th;
     ml[sp] = wml[at];
-    x[sp] = *reinterpret_cast<const v4f *>(wo + at * kDL + 4 * tid);
+    sc[sp] = wsc[at * kMaxWaves + wv];
+    x[sp] = *reinterpret_cast<const v2i *>(wo + at * kDL + 4 * tid);
   }
   float M = -INFINITY;
 #pragma unroll
@@ -488,7 +518,12 @@ __global__ __launch_bounds__(128) void combine_splits_kernel(AttnArgs p, int hea
     for (int sp = 0; sp < kMaxSplits; ++sp) {
       const float e = (sp < S && ml[sp].x != -INFINITY) ? __builtin_amdgcn_exp2f(ml[sp].x - M) : 0.f;
       L = fmaf(e, ml[sp].y, L);
-      acc = acc + e * x[sp];
+      const float f = e * sc[sp];
+      const v4f v = {(float)__builtin_bit_cast(_Float16, (uint16_t)((uint32_t)x[sp][0] & 0xFFFFu)),
+                     (float)__builtin_bit_cast(_Float16, (uint16_t)((uint32_t)x[sp][0] >> 16)),
+                     (float)__builtin_bit_cast(_Float16, (uint16_t)((uint32_t)x[sp][1] & 0xFFFFu)),
+                     (float)__builtin_bit_cast(_Float16, (uint16_t)((uint32_t)x[sp][1] >> 16))};
+      acc = acc + f * v;
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -587,7 +622,9 @@ int attn_splits(const AttnArgs &a) {
 size_t sparse_attn_workspace_bytes(const AttnArgs &a) {
   const int S = attn_splits(a);
   if (S == 1) return 0;
-  return (size_t)S * a.seq.total_q * a.heads * (kDL * sizeof(float) + 2 * sizeof(float));
+  // per (split, token, head): 512 fp16 values, frame and denominator, and
+  // kMaxWaves scales
+  return (size_t)S * a.seq.total_q * a.heads * (kDL * sizeof(uint16_t) + (2 + kMaxWaves) * sizeof(float));
 }
 
 hipError_t launch_sparse_attn(const AttnArgs &args, hipStream_t stream) {
