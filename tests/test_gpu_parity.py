@@ -260,6 +260,46 @@ def test_attention_frame_overflow_recompute():
         H.check_attention_rows(out, lse, q, kv, idx, list(range(T)), [0] * T, scale, 512)
 
 
+@pytest.mark.parametrize("mag", [2.0 ** 20, 2.0 ** -40, 0.0])
+def test_attention_split_partials_extreme_magnitudes(mag):
+    """Few tokens: every token's rows are split over several workgroups,
+    whose partial O is kept in fp16 under a power-of-two scale per (head,
+    wave).  Latent values scaled by 2^20 (partials far beyond fp16's range),
+    by 2^-40 (far below its normal range) and zeroed must come out as the
+    oracle's, relative to the output's own magnitude.  The query is scaled by
+    the inverse power of two, so the logits (and lse) are those of the
+    unscaled case; mag = 0 zeroes the latent part (the rope part still sets
+    the logits) and the output must be exactly zero."""
+    _announce(f"attention split partials, latent x {mag}")
+    T, S, k = 6, 3000, 512
+    q, kv, idx, scale = _attn_case(128, 512, 64, T, S, k, seed=11, scale=1 / math.sqrt(192))
+    q, kv = q.float(), kv.float()
+    if mag > 0:
+        q[:, :, :512] /= mag
+        kv[:, :512] *= mag
+    else:
+        kv[:, :512] = 0.0
+    q, kv = q.to(torch.bfloat16), kv.to(torch.bfloat16)
+    out, lse = _run_attn(q, kv, idx, scale, 512, 64)
+    if mag == 0:
+        assert (out.float() == 0).all() and torch.isfinite(lse).all()
+        return
+    o_gpu = out.cpu().double().numpy()
+    refs, lrefs = [], []
+    for t in range(T):
+        o, l = oracle.sparse_attention_row(q[t].double().numpy(), kv[idx[t].long()].double().numpy(),
+                                           np.arange(k), scale, 512)
+        refs.append(o)
+        lrefs.append(l)
+    ref = np.stack(refs)
+    peak = np.abs(ref).max()
+    # bf16 output rounding (2^-9 relative) plus the fp16 partials (2^-11)
+    assert np.abs(o_gpu - ref).max() <= 2.0 ** -7 * peak
+    assert np.linalg.norm(o_gpu - ref) <= 1e-2 * np.linalg.norm(ref)
+    lref = np.stack(lrefs)
+    assert np.abs(lse.cpu().double().numpy() - lref).max() <= 1e-3 * max(1.0, np.abs(lref).max())
+
+
 @pytest.mark.parametrize("shape", [(8, 64, 16), (16, 128, 32), (128, 512, 64)])
 def test_attention_small_path_shapes(shape):
     H_, dl, dr = shape
