@@ -57,6 +57,10 @@ constexpr int kMaxK = 4096;
 constexpr float kFrameSlack = 32.f;          // log2 headroom above the frame max
 constexpr int kMaxSplits = 4;                // workgroups per token in the split path
 constexpr int kMaxWaves = 4;                 // scales per (split, token, head) in the split path
+// S^T links before the first gather window of a step: kLeadPrefill with one
+// workgroup per token, 0 in the split (few-token) path, whose gathers come
+// from a cache far larger than the MALL and want every cycle of lead time
+constexpr int kLeadPrefill = 10;
 
 // Two floats to fp16 bits (round to nearest even), packed low | high.
 __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
@@ -87,7 +91,7 @@ __device__ __forceinline__ v16f qk_mfma_last_drain(const v16f &acc, const v4i &a
   return r;
 }
 
-template <int NW, bool kPaged>
+template <int NW, bool kPaged, int kGatherLead>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mla_sparse_attn_kernel(AttnArgs p) {
   constexpr int H = NW * 32;
@@ -288,6 +292,16 @@ void mla_sparse_attn_kernel(AttnArgs p) {
     auto step_phase = [&](int tq, const DSA_LDS uint8_t *tbp, const DSA_LDS uint8_t *pbp, bool gnext) {
       constexpr int KS = kD / 16, LA = 3, NPV = 2 * MB * NW;
       static_assert(NPV <= KS, "P.V MFMAs ride along the S^T chain");
+      // Window w of the next tile's gather goes out after link
+      // w * KS / kWindows + kGatherLead of the chain (the last link at the
+      // latest).  Right after the step's barrier its LDS writes land among
+      // the step's first operand reads: on the last 128K chunk a lead of 10
+      // of the 36 links was the fastest (1-3 % per launch); the decode
+      // split path, gathering from HBM, is 2 % faster without a lead.
+      auto gather_link = [](int w) {
+        const int at = w * KS / kWindows + kGatherLead;
+        return at < KS ? at : KS - 1;
+      };
       const DSA_LDS uint8_t *tbq = (const DSA_LDS uint8_t *)kvbuf[tq % kStages];
       GOff src[kRB];
       uint32_t gbase = 0;
@@ -317,7 +331,7 @@ void mla_sparse_attn_kernel(AttnArgs p) {
         if (gnext)
 #pragma unroll
           for (int w = 0; w < kWindows; ++w)
-            if (i == w * KS / kWindows) gather_window(src, gbase, w);
+            if (i == gather_link(w)) gather_window(src, gbase, w);
         __builtin_amdgcn_sched_barrier(0);
       }
       return sc;
@@ -617,6 +631,18 @@ int attn_splits(const AttnArgs &a) {
   return s >= kMaxSplits ? kMaxSplits : (s >= 2 ? 2 : 1);
 }
 
+template <int NW>
+void launch_mla(const AttnArgs &a, bool paged, bool split, dim3 grid, hipStream_t stream) {
+  const dim3 block(NW * 64);
+  if (paged) {
+    if (split) hipLaunchKernelGGL((mla_sparse_attn_kernel<NW, true, 0>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((mla_sparse_attn_kernel<NW, true, kLeadPrefill>), grid, block, 0, stream, a);
+  } else {
+    if (split) hipLaunchKernelGGL((mla_sparse_attn_kernel<NW, false, 0>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((mla_sparse_attn_kernel<NW, false, kLeadPrefill>), grid, block, 0, stream, a);
+  }
+}
+
 }  // namespace
 
 size_t sparse_attn_workspace_bytes(const AttnArgs &a) {
@@ -636,18 +662,16 @@ hipError_t launch_sparse_attn(const AttnArgs &args, hipStream_t stream) {
   const dim3 grid((unsigned)(a.seq.total_q * a.nsplit));
   const bool paged = a.pg.table != nullptr;
   if (mfma_shape(a)) {
+    const bool split = a.nsplit > 1;
     switch (a.heads / 32) {
       case 1:
-        if (paged) hipLaunchKernelGGL((mla_sparse_attn_kernel<1, true>), grid, dim3(64), 0, stream, a);
-        else hipLaunchKernelGGL((mla_sparse_attn_kernel<1, false>), grid, dim3(64), 0, stream, a);
+        launch_mla<1>(a, paged, split, grid, stream);
         break;
       case 2:
-        if (paged) hipLaunchKernelGGL((mla_sparse_attn_kernel<2, true>), grid, dim3(128), 0, stream, a);
-        else hipLaunchKernelGGL((mla_sparse_attn_kernel<2, false>), grid, dim3(128), 0, stream, a);
+        launch_mla<2>(a, paged, split, grid, stream);
         break;
       default:
-        if (paged) hipLaunchKernelGGL((mla_sparse_attn_kernel<4, true>), grid, dim3(256), 0, stream, a);
-        else hipLaunchKernelGGL((mla_sparse_attn_kernel<4, false>), grid, dim3(256), 0, stream, a);
+        launch_mla<4>(a, paged, split, grid, stream);
         break;
     }
     if (a.nsplit > 1)
