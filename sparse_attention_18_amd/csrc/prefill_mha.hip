@@ -412,7 +412,9 @@ void mha_prefill_kernel(MhaArgs p, MhaWs w) {
   // one P was made in) and keep tile t's P for the next step.  One wave's
   // softmax then runs while the other issues MFMAs.  Tile t + 1 is loaded
   // during step t into stage (t + 1) % 3, which step t - 1's P.V (deferred
-  // or not) no longer reads once the step's barrier has passed.
+  // or not) no longer reads once the step's barrier has passed.  A deferred
+  // wave issues those loads after its P.V (which reads stage (t - 1) % 3),
+  // so its MFMAs start right at the barrier.
   const bool defer = wave >= kMWaves / 2;
   v8bf pk[2][2];                  // P of the tile whose P.V is pending
   if (ntiles > 0) issue(tl[0], 0);
@@ -426,8 +428,8 @@ void mha_prefill_kernel(MhaArgs p, MhaWs w) {
     wait_vmcnt<0>();              // this wave's blocks of tile t have landed
     __syncthreads();              // tile t visible; stage (t + 1) % 3 free
     const int st_next = st_cur == kMStages - 1 ? 0 : st_cur + 1;
-    if (t + 1 < ntiles) issue(tl[t + 1], st_next);
     if (defer && t > 0) pv(stage_ptr(st_prev), pk);
+    if (t + 1 < ntiles) issue(tl[t + 1], st_next);
     qk_softmax(stage_ptr(st_cur), pk);
     if (!defer) pv(stage_ptr(st_cur), pk);
     st_prev = st_cur;
