@@ -199,7 +199,11 @@ dsa_status dsa_sparse_attn_prefill(const dsa_problem *p, const uint16_t *q, cons
                                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * The three stages in order (indexer -> top-k -> attention) on one stream.
+ * The three stages in order (indexer -> top-k -> attention) on one stream:
+ * the pipeline of r.nikiv.dev's DeepSeek-V3.2 summary, "How DSA Works" (the
+ * indexer scores every causal key, the 2048 best are kept, attention runs on
+ * those only) and of the ivugangingo.com article, "Sparse attention with
+ * almost linear long-context costs".
  * Arguments as in the stage calls; the results equal the three calls'.  The
  * scores matrix lives at the start of the workspace (ld_scores = max_kv_len
  * rounded up to a multiple of 64); topk_idx_out (nullable) receives the
