@@ -826,7 +826,7 @@ def main():
         log(f"[bench] measured peaks: {peaks}")
     flush = MallFlush(dev)
     wl = wk.CHUNKED_PREFILL_128K
-    bench = value = ms_per_step = stages = roofline = None
+    bench = value = ms_per_step = stages = roofline = topk_plus_attn = None
     if do["prefill"]:
         bench, wl, value, ms_per_step, stages, per_chunk = run_prefill(args, dev, peaks)
         dominant = max(stages, key=lambda s: stages[s]["ms_per_step"])
@@ -837,6 +837,12 @@ def main():
                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE)"}
         if "frac_measured" in d:
             roofline["frac_measured"] = d["frac_measured"]
+        # top-k and sparse attention together: their algorithmic bytes over
+        # their summed time (the two HBM-bound stages of the step)
+        both_ms = stages["topk"]["ms_per_step"] + stages["sparse_attn"]["ms_per_step"]
+        topk_plus_attn = stage_entry(both_ms, stages["topk"]["launches_per_step"] * 2, "hbm",
+                                     topk_bytes(wl, bench.positions) + attn_bytes(wl, bench.positions),
+                                     peaks)
         if args.stages_json:
             with open(args.stages_json, "w") as f:
                 json.dump({"stages": stages, "per_chunk_ms": per_chunk.tolist()}, f, indent=1)
@@ -882,6 +888,7 @@ def main():
         "decode_stages": decode_stages,
         "roofline": roofline,
         "stages": stages,
+        "topk_plus_attn": topk_plus_attn,
         "prefill_configs": prefill_configs or None,
         "measured_peaks": peaks,
         "train_align": train,
